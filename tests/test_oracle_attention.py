@@ -1,0 +1,115 @@
+"""Pins of the oracle's masked attention (CPU only)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention, layout, mask
+
+AR, CH = W.AR_CAUSAL_DM_FULL, W.CHUNK_CAUSAL_KV
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+@pytest.mark.parametrize("case", [
+    dict(nq=9, nk=9, q0=0, mode=AR, n_ar=4),
+    dict(nq=6, nk=11, q0=5, mode=AR, n_ar=7),
+    dict(nq=7, nk=12, q0=5, mode=CH, n_prefix=3, chunk_len=2),
+    dict(nq=4, nk=10, q0=6, mode=CH, n_prefix=6, chunk_len=4),
+])
+def test_vectorised_equals_bruteforce(case):
+    nq, nk, q0, mode = case["nq"], case["nk"], case["q0"], case["mode"]
+    kw = {k: v for k, v in case.items() if k in ("n_ar", "n_prefix", "chunk_len")}
+    h, d = 2, 8
+    q, k, v = _rand((nq, h, d), 1), _rand((nk, h, d), 2), _rand((nk, h, d), 3)
+    o1, l1 = attention.attention(q, k, v, q0, mode, row_block=3, **kw)
+    o2, l2 = attention.attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), q0, mode, **kw)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_tiny_workload_bruteforce_sampled_rows():
+    wl = W.BY_NAME["tiny_fp32"]
+    n = wl.n_tokens
+    n_ar = W.region_counts(wl.segments)[0]
+    q = W.make(0, W.T_Q, (n, 4, 64), "fp32").f32
+    k = W.make(0, W.T_K, (n, 4, 64), "fp32").f32
+    v = W.make(0, W.T_V, (n, 4, 64), "fp32").f32
+    o, _ = attention.attention(q, k, v, 0, AR, n_ar=n_ar)
+    rows = [0, 1, 33, 34, 60, 113]
+    # brute force one row at a time, at its absolute index
+    for r in rows:
+        orow, _ = attention.attention_bruteforce(q[r:r + 1].tolist(), k.tolist(), v.tolist(), r, AR, n_ar=n_ar)
+        np.testing.assert_allclose(o[r], orow[0], rtol=0, atol=1e-12)
+
+
+def test_first_row_reads_only_first_key():
+    q, k, v = _rand((8, 3, 16), 4), _rand((8, 3, 16), 5), _rand((8, 3, 16), 6)
+    o, lse = attention.attention(q, k, v, 0, AR, n_ar=5)
+    np.testing.assert_array_equal(o[0], v[0])
+
+
+def test_zero_query_gives_mean_of_allowed_values():
+    n, n_ar = 12, 5
+    q = np.zeros((n, 2, 8))
+    k, v = _rand((n, 2, 8), 7), _rand((n, 2, 8), 8)
+    o, lse = attention.attention(q, k, v, 0, AR, n_ar=n_ar)
+    for i in range(n):
+        keys = np.arange(i + 1) if i < n_ar else np.arange(n)
+        np.testing.assert_allclose(o[i], v[keys].mean(axis=0), atol=1e-13)
+        np.testing.assert_allclose(lse[:, i], np.log(len(keys)), atol=1e-13)
+
+
+def test_dm_outputs_invariant_to_dm_key_permutation():
+    n, n_ar = 20, 6
+    q, k, v = _rand((n, 2, 8), 9), _rand((n, 2, 8), 10), _rand((n, 2, 8), 11)
+    o, _ = attention.attention(q, k, v, 0, AR, n_ar=n_ar)
+    perm = np.concatenate([np.arange(n_ar), n_ar + np.random.default_rng(0).permutation(n - n_ar)])
+    # permute the DM keys/values only; queries stay in place
+    o2, _ = attention.attention(q, k[perm], v[perm], 0, AR, n_ar=n_ar)
+    np.testing.assert_allclose(o2[n_ar:], o[n_ar:], atol=1e-13)
+
+
+def test_ar_rows_bitwise_invariant_to_dm_perturbation():
+    n, n_ar = 300, 40
+    q, k, v = _rand((n, 2, 16), 12), _rand((n, 2, 16), 13), _rand((n, 2, 16), 14)
+    o, l = attention.attention(q, k, v, 0, AR, n_ar=n_ar)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[n_ar:] += 5
+    k2[n_ar:] *= -3
+    v2[n_ar:] += 100
+    o2, l2 = attention.attention(q2, k2, v2, 0, AR, n_ar=n_ar)
+    np.testing.assert_array_equal(o2[:n_ar], o[:n_ar])
+    np.testing.assert_array_equal(l2[:, :n_ar], l[:, :n_ar])
+    assert not np.allclose(o2[n_ar:], o[n_ar:])
+
+
+def test_chunk_rows_invariant_to_future_chunks():
+    n_prefix, c = 5, 6
+    nk = n_prefix + 4 * c
+    q = _rand((4 * c, 2, 8), 15)
+    k, v = _rand((nk, 2, 8), 16), _rand((nk, 2, 8), 17)
+    o, _ = attention.attention(q, k, v, n_prefix, CH, n_prefix=n_prefix, chunk_len=c)
+    for ch in range(3):
+        cut = n_prefix + (ch + 1) * c
+        k2, v2, q2 = k.copy(), v.copy(), q.copy()
+        k2[cut:] += 3
+        v2[cut:] -= 7
+        q2[(ch + 1) * c:] *= 2
+        o2, _ = attention.attention(q2, k2, v2, n_prefix, CH, n_prefix=n_prefix, chunk_len=c)
+        np.testing.assert_array_equal(o2[:(ch + 1) * c], o[:(ch + 1) * c])
+
+
+def test_rows_helper_matches_full():
+    n, n_ar = 50, 9
+    q, k, v = _rand((n, 3, 8), 18), _rand((n, 3, 8), 19), _rand((n, 3, 8), 20)
+    o, _ = attention.attention(q, k, v, 0, AR, n_ar=n_ar)
+    rows = [0, 8, 9, 49]
+    heads = [0, 2]
+    orow = attention.attention_rows(q[rows], k, v, rows, heads, 0, AR, n_ar=n_ar)
+    np.testing.assert_allclose(orow, o[rows][:, heads], atol=1e-13)
+
+
+def test_flop_count_definition():
+    assert attention.flops(635963395, 24, 128) == pytest.approx(7.815e12, rel=1e-3)
