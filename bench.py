@@ -1,0 +1,172 @@
+"""Benchmark of the MoT joint-attention hot path on one MI355X.
+
+One step = one pass of the whole path over the workload's packed sequence,
+with every input resident in HBM: region-split QKV projection -> mRoPE of K
+(Q is rotated on load) -> masked flash attention -> region-split output
+projection -> flow-matching Euler update of the noisy latent.
+
+Prints ONE JSON line.  ``value`` is masked-attention TFLOP/s counting only
+allowed (query, key, head) triples (4*D flops each) divided by the wall time
+of the whole step, so it is a lower bound on the attention kernel's own rate;
+``roofline`` reports that kernel alone (HIP events on its stream), against
+the MI355X dense bf16 MFMA peak.  ``cpu_baseline`` times the CPU fp64 oracle
+on a bounded sample of the same attention.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def attention_pairs(n, n_ar):
+    """Allowed pairs of the AR-causal / DM-full mask over n tokens: the AR
+    rows see a causal prefix, every DM row sees all n keys."""
+    return n_ar * (n_ar + 1) // 2 + (n - n_ar) * n
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """Time the fp64 oracle attention on a bounded sample: one head, blocks
+    of DM query rows (each reading all keys) until ~budget_s of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import attention as oattn
+
+    n = wl.n_tokens
+    n_ar = W.region_counts(wl.segments)[0]
+    d = wl.head_dim
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((n, 1, d)).astype(np.float32)
+    k = rng.standard_normal((n, 1, d)).astype(np.float32)
+    v = rng.standard_normal((n, 1, d)).astype(np.float32)
+    rows_done = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        while time.perf_counter() - t0 < budget_s and rows_done < n - n_ar:
+            r0 = n_ar + rows_done
+            r1 = min(n, r0 + 256)
+            oattn.attention(q[r0:r1], k, v, r0, W.AR_CAUSAL_DM_FULL, n_ar=n_ar)
+            flops += oattn.flops((r1 - r0) * n, 1, d)
+            rows_done += r1 - r0
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "fp64 oracle attention, 1 of %d heads, %d DM query rows x %d keys "
+                      "(%.1f s wall)" % (wl.n_heads, rows_done, n, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="t2v480p_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the multi-GPU path (head-sharded attention "
+              "behind an all-to-all) is a design, not built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from multimodal_diffusion_transformer_amd import pipeline
+
+    wl = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    n, hid, h, d = wl.n_tokens, wl.hidden, wl.n_heads, wl.head_dim
+    n_ar, n_clean, n_noisy = W.region_counts(wl.segments)
+    X = W.make(wl.wid, W.T_X, (n, hid), wl.dtype)
+    ws = [W.make(wl.wid, W.T_WQKV_AR, (hid, 3 * h * d), wl.dtype, 0.02),
+          W.make(wl.wid, W.T_WQKV_DM, (hid, 3 * h * d), wl.dtype, 0.02),
+          W.make(wl.wid, W.T_WO_AR, (h * d, hid), wl.dtype, 0.02),
+          W.make(wl.wid, W.T_WO_DM, (h * d, hid), wl.dtype, 0.02)]
+    x = W.make(wl.wid, W.T_LATENT, (n_noisy, hid), "fp32")
+    den = pipeline.DenoiserStep(wl, W.to_torch(X), *(W.to_torch(w) for w in ws),
+                                torch.from_numpy(x.f32), device=dev)
+    del X, ws, x
+    sig = (1.0, 0.975)
+
+    stages = ["qkv", "rope_k", "attention", "o_proj", "euler"]
+    fns = [den.project_qkv, den.rope_k, den.attention, den.project_o,
+           lambda: den.euler(*sig)]
+
+    def step(ev=None):
+        for i, f in enumerate(fns):
+            if ev is not None:
+                ev[i][0].record()
+            f()
+            if ev is not None:
+                ev[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in stages] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {name: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1])
+                                for s in range(args.steps)]))
+           for i, name in enumerate(stages)}
+    ms_step = wall * 1e3 / args.steps
+
+    pairs = attention_pairs(n, n_ar)
+    attn_flops = 4.0 * d * h * pairs
+    proj_flops = 2.0 * n * hid * 3 * h * d + 2.0 * n * h * d * hid
+    attn_tflops = attn_flops / (per["attention"] * 1e-3) / 1e12
+    value = attn_flops / (ms_step * 1e-3) / 1e12
+    line = {
+        "metric": "MoT masked-attention TFLOP/s (unmasked pairs) + % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "fp32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, random init)",
+        "config": {"workload": "%s: T2V 480p-shaped packed sequence, %d AR (512 text + EOS + BOG)"
+                               " + %d DM-noisy (16 latent frames x 30x52), %d heads x %d, hidden %d"
+                               % (wl.name, n_ar, n_noisy, h, d, hid) if wl.name == "t2v480p_bf16"
+                   else wl.name,
+                   "tokens": n, "n_ar": n_ar, "n_clean": n_clean, "n_noisy": n_noisy,
+                   "heads": h, "head_dim": d, "hidden": hid, "mask": "AR_CAUSAL_DM_FULL",
+                   "step": "qkv_proj + mrope(K; Q on load) + attention + o_proj + euler"},
+        "pct_of_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "attention_kernel_tflops": round(attn_tflops, 2),
+        "step_tflops_all_contractions": round((attn_flops + proj_flops) / (ms_step * 1e-3) / 1e12, 2),
+        "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * motattn — the joint-attention hot path of the Cosmos 3 Mixture-of-
+ * Transformers denoiser forward pass, as hand-written HIP kernels for
+ * gfx950 (MI355X), behind a plain C ABI.
+ *
+ * Sources (pages, by title and section):
+ *   "Cosmos 3 方法原理全解" (Cosmos 3 method explained):
+ *       §2 packed sequence S = [S_AR, S_DM] and its DM order,
+ *       §3 the two MoT rooms and the joint-attention equations O_AR / O_DM,
+ *       §5 3D mRoPE coordinates, Δt = 6/TPS, the AR->DM time gap,
+ *       §7.2 the Euler sampler update.
+ *   "NVIDIA 发布 Cosmos 3 系列四个开放权重世界模型" (four new checkpoints),
+ *       section "流式生成如何工作": chunk-causal attention against a
+ *       key/value cache.
+ *
+ * Conventions shared by every call:
+ *   - Every call returns a mot_status.  Argument checks run on the host
+ *     before any launch; on MOT_ERR_INVALID_ARG / MOT_ERR_UNSUPPORTED
+ *     nothing was enqueued.  MOT_ERR_HIP reports a failed launch.  Outputs
+ *     are undefined after any status other than MOT_OK.
+ *   - Device pointers are caller-owned device memory (e.g. torch tensors).
+ *     The library allocates no device memory and keeps no mutable global
+ *     state; calls are thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device calls only enqueue work on it; they never synchronize.
+ *   - bf16 is bfloat16 (1-8-7), stored as 16-bit words; fp32 is IEEE float.
+ *   - Strides are in elements.  Device pointers must be 16-byte aligned and
+ *     strides multiples of 8 elements (bf16) / 4 elements (fp32) unless a
+ *     call says otherwise.
+ */
+#ifndef MOTATTN_H
+#define MOTATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOT_ABI_VERSION 1
+
+typedef enum {
+  MOT_OK = 0,
+  MOT_ERR_INVALID_ARG = 1,
+  MOT_ERR_UNSUPPORTED = 2,
+  MOT_ERR_HIP = 3
+} mot_status;
+
+typedef enum { MOT_BF16 = 0, MOT_FP32 = 1 } mot_dtype;
+
+typedef enum {
+  MOT_AR_CAUSAL_DM_FULL = 0, /* method page §3: AR causal, DM reads all */
+  MOT_CHUNK_CAUSAL_KV = 1    /* streaming page: prefix + chunk-causal  */
+} mot_mask_mode;
+
+typedef enum { MOT_REGION_AR = 0, MOT_REGION_DM_CLEAN = 1, MOT_REGION_DM_NOISY = 2 } mot_region;
+
+typedef enum {
+  MOT_KIND_TEXT = 0, MOT_KIND_SPECIAL = 1, MOT_KIND_VIDEO = 2,
+  MOT_KIND_AUDIO = 3, MOT_KIND_ACTION = 4, MOT_KIND_PROPRIO = 5
+} mot_kind;
+
+/* One group of tokens of the packed sequence (method page §2).
+ * n_tokens: TEXT / SPECIAL / AUDIO / ACTION / PROPRIO token count.
+ * VIDEO: n_frames latent frames x n_views views x grid_h x grid_w.
+ * rate: tokens per second (AUDIO / ACTION) or pixel FPS (VIDEO).
+ * frame0: VIDEO absolute first latent frame, or -1 to continue the count.
+ * step0: AUDIO / ACTION index of the first token on its time ladder. */
+typedef struct {
+  int32_t region; /* mot_region */
+  int32_t kind;   /* mot_kind   */
+  int64_t n_tokens;
+  int64_t n_frames;
+  int64_t n_views;
+  int64_t grid_h;
+  int64_t grid_w;
+  double rate;
+  int64_t frame0;
+  int64_t step0;
+} mot_segment;
+
+int mot_abi_version(void);
+const char* mot_status_string(mot_status s);
+
+/* Packed-sequence layout (method page §2 and §5), host only.
+ * Writes per-token region tags (uint8, mot_region) and (t, h, w) positions
+ * (float32 [N][3]) into caller-owned HOST buffers of `capacity` tokens.
+ * Text/special tokens: t = h = w = running AR index.  DM origin
+ * t0 = n_ar + 15000.  A token k on a ladder of rate TPS sits at
+ * t0 + (6.0*k)/TPS evaluated in double and rounded once to float (video
+ * uses TPS = FPS/4 and k = absolute latent frame); audio/action h = w = 0;
+ * proprio at t0; video h = row, w = view*grid_w + col, ordered
+ * frame -> view -> row -> col.
+ * Errors: INVALID_ARG for null pointers, bad enums, empty segments, a
+ * segment order that breaks §2 (AR, then clean, then noisy; vision, audio,
+ * action inside a DM group) or N > capacity.  When the segments are valid,
+ * *n_tok_out and *n_ar_out receive N and n_ar even if N > capacity, so a
+ * first call with capacity 0 (buffers may then be NULL) sizes the buffers;
+ * otherwise they receive 0. */
+mot_status mot_build_layout(const mot_segment* segs, int32_t n_segs, int64_t capacity,
+                            int64_t* n_tok_out, int64_t* n_ar_out,
+                            float* pos_thw_host, uint8_t* region_host);
+
+/* Region-split projection (method page §3, §3.2: Reasoner weights for AR
+ * rows, Generator weights for DM rows):
+ *     Y[r, :] = X[r, :] @ (r < n_ar ? W_ar : W_dm)
+ * x: [n_rows, d_in] row-major, dtype in_dt.  w_ar, w_dm: [d_in, d_out]
+ * row-major, dtype in_dt.  y: [n_rows, d_out] row-major, dtype out_dt.
+ * Used for the fused QKV projection (d_out = 3*H*D, columns [Q|K|V], each
+ * [H][D]) and for the output projection.  bf16 inputs accumulate in fp32 on
+ * MFMA; a bf16 output is the round-to-nearest-even of the fp32 result.
+ * fp32 inputs are computed in fp32.  Supported: in_dt == MOT_BF16 with
+ * d_in % 64 == 0 and d_out % 64 == 0, or in_dt == MOT_FP32 (any sizes).
+ * 0 <= n_ar <= n_rows; n_rows == 0 is a no-op.  y must not alias x or w. */
+mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, void* y,
+                           int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
+                           mot_dtype in_dt, mot_dtype out_dt, void* stream);
+
+/* Unified 3D mRoPE (method page §5), in place on x [n_tok][n_heads][head_dim]
+ * with element strides tok_stride / head_stride (the last dim contiguous).
+ * pos_thw: device float32 [n_tok][3].  Pair k of P = head_dim/2 rotates
+ * (x_k, x_{k+P}) by a = pos[axis(k)] * theta^(-2k/head_dim), axis = t for
+ * k < sec_t, h for k < sec_t+sec_h, w otherwise.  Angles and their cos/sin
+ * are evaluated in fp64, the rotation in fp32, the store rounds RNE.
+ * head_dim in {64, 128}; sec_t+sec_h+sec_w == head_dim/2; all >= 0. */
+mot_status mrope_apply(void* x, mot_dtype dt, int64_t n_tok, int32_t n_heads, int32_t head_dim,
+                       int64_t tok_stride, int64_t head_stride, const float* pos_thw,
+                       int32_t sec_t, int32_t sec_h, int32_t sec_w, float theta, void* stream);
+
+/* Arguments of the masked attention.  Query row r has absolute index
+ * i = q0 + r in key space.  Masks (i: query, j: key):
+ *   MOT_AR_CAUSAL_DM_FULL (method page §3):  i >= n_ar  or  j <= i
+ *   MOT_CHUNK_CAUSAL_KV (streaming page):   j < n_prefix  or
+ *        floor((j-n_prefix)/chunk_len) <= floor((i-n_prefix)/chunk_len)
+ * q: [nq][H][D], k, v: [nk][H][D], o: [nq][H][D] with the given token and
+ * head strides (elements, last dim contiguous).  lse (nullable): fp32
+ * [H][nq], natural-log sum-exp of the scaled scores.  q_pos / k_pos
+ * (nullable, device fp32 [nq][3] / [nk][3]): when set, Q / K are rotated by
+ * mRoPE (sec_*, theta) as their tiles are loaded; otherwise they are used as
+ * given.  scale == 0 means 1/sqrt(D). */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int32_t dt;        /* mot_dtype of q, k, v and o */
+  int32_t n_heads;
+  int32_t head_dim;  /* 64 or 128 */
+  int32_t mask;      /* mot_mask_mode */
+  int64_t nq, nk, q0;
+  int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs;
+  int64_t n_ar;
+  int64_t n_prefix, chunk_len;
+  const float* q_pos;
+  const float* k_pos;
+  int32_t sec_t, sec_h, sec_w;
+  float theta;
+  float scale;
+} mot_attn_args;
+
+/* Flash-style masked attention, O = softmax(mask(Q K^T * scale)) V per head
+ * (method page §3 equations; streaming page for the chunk mode).  bf16 runs
+ * on MFMA with fp32 online softmax and skips tiles with no allowed pair;
+ * fp32 runs on the vector ALUs in fp32.  Requires nq >= 1, nk >= q0 + nq in
+ * AR mode (every query sees its diagonal), q0 >= n_prefix and chunk_len >= 1
+ * in chunk mode, 0 <= n_ar, n_prefix <= nk. */
+mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
+
+/* Flow-matching Euler update (method page §7.2), in place:
+ *     x[e] = x[e] + (sigma_next - sigma) * v[e],   e < n
+ * x: device fp32; v: device bf16 or fp32 (v_dt), contiguous.  The step
+ * (sigma_next - sigma) is formed in fp32 and applied with one fused
+ * multiply-add.  x_bf16 (nullable): also store bf16(x_new) there (the row
+ * block of the next step's packed input).  n == 0 is a no-op. */
+mot_status flow_euler_step(float* x, const void* v, mot_dtype v_dt, int64_t n,
+                           float sigma, float sigma_next, void* x_bf16, void* stream);
+
+/* Debug/test helpers: the exact mask and the tile classes the attention
+ * kernel uses.  mask_dev: device uint8 [nq][nk] (1 = allowed), nullable.
+ * tiles_dev: device uint8 [ceil(nq/bm)][ceil(nk/bn)] (0 empty, 1 partial,
+ * 2 full, judged on in-range pairs), nullable.  Only the mask fields of
+ * args (mask, nq, nk, q0, n_ar, n_prefix, chunk_len) are read. */
+mot_status mot_mask_materialize(const mot_attn_args* args, uint8_t* mask_dev, int32_t bm,
+                                int32_t bn, uint8_t* tiles_dev, void* stream);
+
+/* Host version of the tile classifier, into a HOST buffer. */
+mot_status mot_tile_classes_host(const mot_attn_args* args, int32_t bm, int32_t bn,
+                                 uint8_t* tiles_host);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOTATTN_H */

@@ -1,0 +1,147 @@
+// C ABI entry points that validate, then dispatch to the kernels:
+// version and status strings, masked attention, region-split projection,
+// and the mask / tile-class materialisers used by the tests.
+#include <math.h>
+
+#include "common.hpp"
+#include "rope_dev.hpp"
+
+namespace mot {
+hipError_t attention_bf16_mfma(const mot_attn_args* a, const RopeTable& rt, hipStream_t s);
+hipError_t attention_f32_valu(const mot_attn_args* a, const RopeTable& rt, hipStream_t s);
+hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* y, int64_t n_rows,
+                       int64_t n_ar, int64_t K, int64_t N, mot_dtype in_dt, mot_dtype out_dt,
+                       hipStream_t s);
+
+static MaskSpec mask_of(const mot_attn_args* a) {
+  MaskSpec m;
+  m.mode = a->mask; m.nq = a->nq; m.nk = a->nk; m.q0 = a->q0;
+  m.n_ar = a->n_ar; m.n_prefix = a->n_prefix; m.chunk_len = a->chunk_len > 0 ? a->chunk_len : 1;
+  return m;
+}
+
+static bool mask_args_ok(const mot_attn_args* a) {
+  if (a->nq < 1 || a->nk < 1 || a->q0 < 0) return false;
+  if (a->mask == MOT_AR_CAUSAL_DM_FULL) {
+    if (a->n_ar < 0 || a->n_ar > a->nk) return false;
+    if (a->nk < a->q0 + a->nq) return false;  // every query sees its diagonal
+    return true;
+  }
+  if (a->mask == MOT_CHUNK_CAUSAL_KV) {
+    if (a->chunk_len < 1 || a->n_prefix < 0 || a->n_prefix > a->nk) return false;
+    if (a->q0 < a->n_prefix) return false;
+    return true;
+  }
+  return false;
+}
+
+__global__ void mask_kernel(MaskSpec m, uint8_t* out) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= m.nq * m.nk) return;
+  int64_t r = e / m.nk, j = e % m.nk;
+  out[e] = mask_allowed(m, m.q0 + r, j) ? 1 : 0;
+}
+
+__host__ __device__ inline uint8_t classify(const MaskSpec& m, int bm, int bn, int64_t tq, int64_t tk) {
+  int64_t ra = tq * bm, rb = ra + bm - 1 < m.nq ? ra + bm - 1 : m.nq - 1;
+  int64_t ja = tk * bn, jb = ja + bn - 1 < m.nk ? ja + bn - 1 : m.nk - 1;
+  return (uint8_t)tile_class(m, m.q0 + ra, m.q0 + rb, ja, jb);
+}
+
+__global__ void tile_kernel(MaskSpec m, int bm, int bn, int64_t ntq, int64_t ntk, uint8_t* out) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= ntq * ntk) return;
+  out[e] = classify(m, bm, bn, e / ntk, e % ntk);
+}
+
+}  // namespace mot
+
+using namespace mot;
+
+extern "C" int mot_abi_version(void) { return MOT_ABI_VERSION; }
+
+extern "C" const char* mot_status_string(mot_status s) {
+  switch (s) {
+    case MOT_OK: return "ok";
+    case MOT_ERR_INVALID_ARG: return "invalid argument";
+    case MOT_ERR_UNSUPPORTED: return "unsupported combination";
+    case MOT_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" mot_status mot_attention_fwd(const mot_attn_args* a, void* stream) {
+  if (!a) return MOT_ERR_INVALID_ARG;
+  if (!a->q || !a->k || !a->v || !a->o) return MOT_ERR_INVALID_ARG;
+  if (a->n_heads <= 0 || (a->head_dim != 64 && a->head_dim != 128)) return MOT_ERR_INVALID_ARG;
+  if (a->dt != MOT_BF16 && a->dt != MOT_FP32) return MOT_ERR_INVALID_ARG;
+  if (!mask_args_ok(a)) return MOT_ERR_INVALID_ARG;
+  if (!(a->scale >= 0.f) || !isfinite(a->scale)) return MOT_ERR_INVALID_ARG;
+  const int64_t al = a->dt == MOT_BF16 ? 8 : 4;
+  const int64_t st[8] = {a->q_ts, a->q_hs, a->k_ts, a->k_hs, a->v_ts, a->v_hs, a->o_ts, a->o_hs};
+  for (int i = 0; i < 8; ++i)
+    if (st[i] <= 0 || st[i] % al) return MOT_ERR_INVALID_ARG;
+  if (((uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v | (uintptr_t)a->o) & 15)
+    return MOT_ERR_INVALID_ARG;
+  if ((uintptr_t)a->lse & 3) return MOT_ERR_INVALID_ARG;
+  RopeTable rt;
+  rt.sec_t = a->sec_t;
+  rt.sec_th = a->sec_t + a->sec_h;
+  if (a->q_pos || a->k_pos) {
+    if (a->sec_t < 0 || a->sec_h < 0 || a->sec_w < 0 ||
+        a->sec_t + a->sec_h + a->sec_w != a->head_dim / 2 || !(a->theta > 0.f))
+      return MOT_ERR_INVALID_ARG;
+    if (((uintptr_t)a->q_pos | (uintptr_t)a->k_pos) & 3) return MOT_ERR_INVALID_ARG;
+    for (int k = 0; k < a->head_dim / 2; ++k)
+      rt.inv_freq[k] = pow((double)a->theta, -2.0 * k / a->head_dim);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = a->dt == MOT_BF16 ? attention_bf16_mfma(a, rt, s) : attention_f32_valu(a, rt, s);
+  return e == hipSuccess ? MOT_OK : MOT_ERR_HIP;
+}
+
+extern "C" mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, void* y,
+                                      int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
+                                      mot_dtype in_dt, mot_dtype out_dt, void* stream) {
+  if (n_rows < 0 || n_ar < 0 || n_ar > n_rows || d_in <= 0 || d_out <= 0) return MOT_ERR_INVALID_ARG;
+  if (n_rows == 0) return MOT_OK;
+  if (!x || !y || (n_ar > 0 && !w_ar) || (n_ar < n_rows && !w_dm)) return MOT_ERR_INVALID_ARG;
+  if ((in_dt != MOT_BF16 && in_dt != MOT_FP32) || (out_dt != MOT_BF16 && out_dt != MOT_FP32))
+    return MOT_ERR_INVALID_ARG;
+  if (((uintptr_t)x | (uintptr_t)w_ar | (uintptr_t)w_dm | (uintptr_t)y) & 15) return MOT_ERR_INVALID_ARG;
+  if (in_dt == MOT_BF16 && (d_in % 64 || d_out % 64)) return MOT_ERR_UNSUPPORTED;
+  if (in_dt == MOT_FP32 && out_dt != MOT_FP32) return MOT_ERR_UNSUPPORTED;
+  hipError_t e = region_gemm(x, w_ar, w_dm, y, n_rows, n_ar, d_in, d_out, in_dt, out_dt,
+                             (hipStream_t)stream);
+  return e == hipSuccess ? MOT_OK : MOT_ERR_HIP;
+}
+
+extern "C" mot_status mot_mask_materialize(const mot_attn_args* a, uint8_t* mask_dev, int32_t bm,
+                                           int32_t bn, uint8_t* tiles_dev, void* stream) {
+  if (!a || !mask_args_ok(a)) return MOT_ERR_INVALID_ARG;
+  if (tiles_dev && (bm <= 0 || bn <= 0)) return MOT_ERR_INVALID_ARG;
+  MaskSpec m = mask_of(a);
+  hipStream_t s = (hipStream_t)stream;
+  if (mask_dev) {
+    int64_t n = m.nq * m.nk;
+    hipLaunchKernelGGL(mask_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, m, mask_dev);
+    MOT_CHECK_LAUNCH();
+  }
+  if (tiles_dev) {
+    int64_t ntq = (m.nq + bm - 1) / bm, ntk = (m.nk + bn - 1) / bn;
+    hipLaunchKernelGGL(tile_kernel, dim3((unsigned)((ntq * ntk + 255) / 256)), dim3(256), 0, s, m, bm,
+                       bn, ntq, ntk, tiles_dev);
+    MOT_CHECK_LAUNCH();
+  }
+  return MOT_OK;
+}
+
+extern "C" mot_status mot_tile_classes_host(const mot_attn_args* a, int32_t bm, int32_t bn,
+                                            uint8_t* tiles_host) {
+  if (!a || !tiles_host || bm <= 0 || bn <= 0 || !mask_args_ok(a)) return MOT_ERR_INVALID_ARG;
+  MaskSpec m = mask_of(a);
+  int64_t ntq = (m.nq + bm - 1) / bm, ntk = (m.nk + bn - 1) / bn;
+  for (int64_t tq = 0; tq < ntq; ++tq)
+    for (int64_t tk = 0; tk < ntk; ++tk) tiles_host[tq * ntk + tk] = classify(m, bm, bn, tq, tk);
+  return MOT_OK;
+}

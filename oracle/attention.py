@@ -63,6 +63,8 @@ def attention_rows(q_rows, k, v, rows, heads, q0, mode, n_ar=0, n_prefix=0,
 
     q_rows [len(rows), H, D] holds the query vectors of ``rows`` (indices
     into the query block); returns O [len(rows), len(heads), D] float64.
+    Rows whose allowed key sets are identical are evaluated together (the
+    same definition, one matrix product per group).
     """
     q_rows = np.asarray(q_rows, dtype=np.float64)
     d = q_rows.shape[-1]
@@ -71,15 +73,21 @@ def attention_rows(q_rows, k, v, rows, heads, q0, mode, n_ar=0, n_prefix=0,
     nk = k.shape[0]
     out = np.empty((len(rows), len(heads), d), dtype=np.float64)
     j = np.arange(nk, dtype=np.int64)
+    groups = {}
     for a, r in enumerate(rows):
         allow = _mask.allowed(q0 + int(r), j, mode, n_ar, n_prefix, chunk_len)
         idx = np.nonzero(allow)[0]
-        for b, h in enumerate(heads):
-            kk = np.asarray(k[idx, h, :], dtype=np.float64)
-            vv = np.asarray(v[idx, h, :], dtype=np.float64)
-            s = (kk @ q_rows[a, h, :]) * scale
-            p = np.exp(s - s.max())
-            out[a, b, :] = (p @ vv) / p.sum()
+        key = ("prefix", len(idx)) if idx[-1] + 1 == len(idx) else ("row", a)
+        groups.setdefault(key, (idx, []))[1].append(a)
+    for b, h in enumerate(heads):
+        kh = np.asarray(k[:, h, :], dtype=np.float64)
+        vh = np.asarray(v[:, h, :], dtype=np.float64)
+        for key, (idx, members) in groups.items():
+            kk = kh[:len(idx)] if key[0] == "prefix" else kh[idx]
+            vv = vh[:len(idx)] if key[0] == "prefix" else vh[idx]
+            s = (q_rows[members, h, :] @ kk.T) * scale
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[members, b, :] = (p @ vv) / p.sum(axis=1, keepdims=True)
     return out
 
 

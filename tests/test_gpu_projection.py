@@ -1,0 +1,106 @@
+"""GPU parity of the region-split projection mot_qkv_project."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import projection as oproj
+from tests.gpu_util import assert_parity, device, say, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _mot():
+    import multimodal_diffusion_transformer_amd as mot
+    return mot
+
+
+CASES = [
+    # name, n_rows, n_ar, d_in, d_out
+    ("boundary_mid_tile", 300, 130, 256, 384),
+    ("all_ar", 129, 129, 128, 128),
+    ("all_dm", 200, 0, 192, 320),
+    ("ragged_cols_64", 260, 70, 64, 64 * 3),
+    ("qkv_policy_shape", 2451, 258, 3072, 9216),
+    ("o_policy_shape", 2451, 258, 3072, 3072),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_projection_bf16_parity_and_rne_store(case):
+    name, n, n_ar, d_in, d_out = case
+    dev = device()
+    mot = _mot()
+    say("projection %s %dx%d -> %d (n_ar=%d)" % (name, n, d_in, d_out, n_ar))
+    x = W.make(20, W.T_X, (n, d_in), "bf16")
+    wa = W.make(20, W.T_WQKV_AR, (d_in, d_out), "bf16", 0.02)
+    wd = W.make(20, W.T_WQKV_DM, (d_in, d_out), "bf16", 0.02)
+    X, WA, WD = (W.to_torch(t, dev) for t in (x, wa, wd))
+    Y32 = torch.empty((n, d_out), dtype=torch.float32, device=dev)
+    Y16 = torch.empty((n, d_out), dtype=torch.bfloat16, device=dev)
+    mot.mot_qkv_project(X, WA, WD, Y32, n_ar)
+    mot.mot_qkv_project(X, WA, WD, Y16, n_ar)
+    torch.cuda.synchronize()
+    y32 = to_np(Y32)
+    rows = np.arange(n) if n <= 400 else np.unique(np.r_[0:n_ar + 2, np.random.default_rng(0).choice(n, 64)])
+    want = np.empty((len(rows), d_out))
+    for a, r in enumerate(rows):
+        w = wa.f32 if r < n_ar else wd.f32
+        want[a] = oproj.project_rows(x.f32[r:r + 1], w)[0]
+    assert_parity(y32[rows], want, "fp32" if d_in <= 256 else "bf16", name)
+    np.testing.assert_array_equal(Y16.cpu().view(torch.int16).numpy().view(np.uint16),
+                                  W.bf16_bits(y32))
+
+
+def test_projection_fp32_tiny_workload():
+    dev = device()
+    mot = _mot()
+    wl = W.BY_NAME["tiny_fp32"]
+    n, n_ar = wl.n_tokens, W.region_counts(wl.segments)[0]
+    x = W.make(0, W.T_X, (n, 256), "fp32")
+    wa = W.make(0, W.T_WQKV_AR, (256, 768), "fp32", 0.02)
+    wd = W.make(0, W.T_WQKV_DM, (256, 768), "fp32", 0.02)
+    Y = torch.empty((n, 768), dtype=torch.float32, device=dev)
+    mot.mot_qkv_project(*(W.to_torch(t, dev) for t in (x, wa, wd)), Y, n_ar)
+    torch.cuda.synchronize()
+    want = oproj.project(x.f32, wa.f32, wd.f32, n_ar)
+    assert_parity(to_np(Y), want, "fp32", "tiny fp32 qkv")
+
+
+def test_projection_ar_rows_ignore_generator_weights():
+    dev = device()
+    mot = _mot()
+    n, n_ar, d = 500, 258, 256
+    x = W.make(21, 0, (n, d), "bf16")
+    wa = W.make(21, 1, (d, 512), "bf16", 0.02)
+    wd = W.make(21, 2, (d, 512), "bf16", 0.02)
+    X, WA, WD = (W.to_torch(t, dev) for t in (x, wa, wd))
+    Y1 = torch.empty((n, 512), dtype=torch.bfloat16, device=dev)
+    Y2 = torch.empty_like(Y1)
+    mot.mot_qkv_project(X, WA, WD, Y1, n_ar)
+    mot.mot_qkv_project(X, WA, (WD * 3).contiguous(), Y2, n_ar)
+    torch.cuda.synchronize()
+    a, b = Y1.cpu().view(torch.int16), Y2.cpu().view(torch.int16)
+    assert torch.equal(a[:n_ar], b[:n_ar]) and not torch.equal(a[n_ar:], b[n_ar:])
+
+
+def test_projection_long_workload_qkv_sampled_rows():
+    dev = device()
+    mot = _mot()
+    wl = W.BY_NAME["t2v480p_long_bf16"]
+    n, n_ar = wl.n_tokens, W.region_counts(wl.segments)[0]
+    hid = wl.hidden
+    dout = 3 * wl.n_heads * wl.head_dim
+    say("projection long workload %d x %d -> %d" % (n, hid, dout))
+    x = W.make(wl.wid, W.T_X, (n, hid), "bf16")
+    wa = W.make(wl.wid, W.T_WQKV_AR, (hid, dout), "bf16", 0.02)
+    wd = W.make(wl.wid, W.T_WQKV_DM, (hid, dout), "bf16", 0.02)
+    Y = torch.empty((n, dout), dtype=torch.float32, device=dev)
+    mot.mot_qkv_project(*(W.to_torch(t, dev) for t in (x, wa, wd)), Y, n_ar)
+    torch.cuda.synchronize()
+    rows = np.unique(np.r_[0, 1, n_ar - 1, n_ar, n_ar + 1, n - 1,
+                           np.random.default_rng(1).choice(n, 40)])
+    got = to_np(Y[torch.from_numpy(rows).to(dev)])
+    want = np.stack([oproj.project_rows(x.f32[r:r + 1], wa.f32 if r < n_ar else wd.f32)[0]
+                     for r in rows])
+    assert_parity(got, want, "bf16", "long qkv sampled")

@@ -1,0 +1,153 @@
+"""CPU tests of the C-ABI library: it loads, exports what the header
+declares, and its host-side logic (layout, tile classifier, argument checks)
+matches the oracle exactly.  No device work is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import layout as olayout
+from oracle import mask as omask
+
+mot = pytest.importorskip("multimodal_diffusion_transformer_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "motattn.h")
+
+
+def _declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:mot_status|int|const char\*)\s+(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary_calls():
+    names = _declared_functions()
+    for n in ("mot_qkv_project", "mrope_apply", "mot_attention_fwd", "flow_euler_step"):
+        assert n in names
+    assert sorted(names) == sorted(mot.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mot.LIB_PATH)
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", mot.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(_declared_functions()) <= exported
+
+
+def test_abi_version_and_status_strings():
+    assert mot.mot_abi_version() == 1
+    assert mot.mot_status_string(0) == "ok"
+    assert "invalid" in mot.mot_status_string(1)
+
+
+@pytest.mark.parametrize("wl", W.WORKLOADS, ids=lambda w: w.name)
+def test_layout_bitwise_equals_oracle(wl):
+    p1, r1, a1 = mot.mot_build_layout(wl.segments)
+    p2, r2, a2 = olayout.build(wl.segments)
+    assert a1 == a2
+    np.testing.assert_array_equal(r1, r2)
+    np.testing.assert_array_equal(p1.view(np.uint32), p2.view(np.uint32))
+
+
+def test_layout_bitwise_on_mixed_rates():
+    segs = [W.text(5), *W.eos_bog(), W.video(W.DM_CLEAN, 2, 2, 3, 4, fps=30.0),
+            W.audio(W.DM_CLEAN, 17), W.action(W.DM_CLEAN, 9, hz=15.0),
+            W.video(W.DM_NOISY, 3, 2, 3, 4, fps=30.0), W.audio(W.DM_NOISY, 33, step0=17),
+            W.action(W.DM_NOISY, 21, hz=10.0, step0=9), W.proprio(W.DM_NOISY, 2)]
+    p1, r1, a1 = mot.mot_build_layout(segs)
+    p2, r2, a2 = olayout.build(segs)
+    np.testing.assert_array_equal(p1.view(np.uint32), p2.view(np.uint32))
+    np.testing.assert_array_equal(r1, r2)
+
+
+@pytest.mark.parametrize("segs", [
+    [W.text(3), W.video(W.DM_NOISY, 1, 1, 2, 2), W.video(W.DM_CLEAN, 1, 1, 2, 2)],
+    [W.text(3), W.action(W.DM_NOISY, 2), W.video(W.DM_NOISY, 1, 1, 2, 2)],
+    [W.text(3), W.video(W.DM_NOISY, 1, 1, 2, 2), W.text(2)],
+    [W.text(0)],
+])
+def test_layout_rejects_bad_order(segs):
+    with pytest.raises(mot.MotError):
+        mot.mot_build_layout(segs)
+
+
+@pytest.mark.parametrize("case", [
+    dict(nq=25474, nk=25474, q0=0, mask=W.AR_CAUSAL_DM_FULL, n_ar=514),
+    dict(nq=2451, nk=2451, q0=0, mask=W.AR_CAUSAL_DM_FULL, n_ar=258),
+    dict(nq=300, nk=700, q0=400, mask=W.AR_CAUSAL_DM_FULL, n_ar=513),
+    dict(nq=1440, nk=13218, q0=11778, mask=W.CHUNK_CAUSAL_KV, n_prefix=258, chunk_len=1440),
+    dict(nq=3 * 37 + 5, nk=258 + 3 * 37 + 5, q0=258, mask=W.CHUNK_CAUSAL_KV, n_prefix=258, chunk_len=37),
+])
+@pytest.mark.parametrize("bm,bn", [(128, 64), (128, 128), (32, 64)])
+def test_host_tile_classes_equal_oracle(case, bm, bn):
+    a = mot.mask_args(**case)
+    got = mot.mot_tile_classes_host(a, bm, bn)
+    m = omask.materialize(case["nq"], case["nk"], case["q0"], case["mask"],
+                          case.get("n_ar", 0), case.get("n_prefix", 0), case.get("chunk_len", 1))
+    want = omask.tile_classes(m, bm, bn)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_tile_counts_t2v480p_at_128():
+    a = mot.mask_args(25474, 25474, 0, W.AR_CAUSAL_DM_FULL, n_ar=514)
+    tc = mot.mot_tile_classes_host(a, 128, 128)
+    assert tc.size == 200 * 200
+    assert int((tc == omask.EMPTY).sum()) == 790 and int((tc == omask.PARTIAL).sum()) == 200
+
+
+# ---- argument checks: every one returns before any launch ----
+def _args(**kw):
+    a = mot.mot_attn_args()
+    a.q = a.k = a.v = a.o = 4096
+    a.dt, a.n_heads, a.head_dim, a.mask = mot.MOT_BF16, 2, 128, mot.MOT_AR_CAUSAL_DM_FULL
+    a.nq = a.nk = 64
+    a.q_ts = a.k_ts = a.v_ts = a.o_ts = 256
+    a.q_hs = a.k_hs = a.v_hs = a.o_hs = 128
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q=None), dict(head_dim=96), dict(n_heads=0), dict(nq=0), dict(nk=10),
+    dict(q_ts=7), dict(o_hs=0), dict(q=4100), dict(dt=5), dict(mask=7),
+    dict(mask=mot.MOT_CHUNK_CAUSAL_KV, chunk_len=0),
+    dict(mask=mot.MOT_CHUNK_CAUSAL_KV, chunk_len=8, n_prefix=10, q0=5, nk=100),
+    dict(q_pos=4096, sec_t=1, sec_h=1, sec_w=1),
+    dict(scale=-1.0),
+])
+def test_attention_rejects_bad_args(kw):
+    st = mot.raw_call("mot_attention_fwd", ctypes.byref(_args(**kw)), None)
+    assert st == mot.MOT_ERR_INVALID_ARG
+
+
+def test_projection_and_rope_and_euler_reject_bad_args():
+    vp = ctypes.c_void_p
+    # projection: n_ar > n_rows; unaligned; bf16 with d_in not a multiple of 64
+    assert mot.raw_call("mot_qkv_project", vp(4096), vp(4096), vp(4096), vp(4096), 10, 11, 64,
+                        64, 0, 0, None) == mot.MOT_ERR_INVALID_ARG
+    assert mot.raw_call("mot_qkv_project", vp(4098), vp(4096), vp(4096), vp(4096), 10, 5, 64,
+                        64, 0, 0, None) == mot.MOT_ERR_INVALID_ARG
+    assert mot.raw_call("mot_qkv_project", vp(4096), vp(4096), vp(4096), vp(4096), 10, 5, 96,
+                        64, 0, 0, None) == mot.MOT_ERR_UNSUPPORTED
+    # rope: sections that do not cover D/2; head_dim 96
+    assert mot.raw_call("mrope_apply", vp(4096), 0, 10, 2, 128, 256, 128, vp(4096), 16, 24, 23,
+                        ctypes.c_float(1e4), None) == mot.MOT_ERR_INVALID_ARG
+    assert mot.raw_call("mrope_apply", vp(4096), 0, 10, 2, 96, 256, 128, vp(4096), 16, 16, 16,
+                        ctypes.c_float(1e4), None) == mot.MOT_ERR_INVALID_ARG
+    # euler: negative n; unaligned v; zero n is a no-op
+    assert mot.raw_call("flow_euler_step", vp(4096), vp(4096), 0, -1, ctypes.c_float(1.0),
+                        ctypes.c_float(0.5), None, None) == mot.MOT_ERR_INVALID_ARG
+    assert mot.raw_call("flow_euler_step", vp(4096), vp(4098), 0, 64, ctypes.c_float(1.0),
+                        ctypes.c_float(0.5), None, None) == mot.MOT_ERR_INVALID_ARG
+    assert mot.raw_call("flow_euler_step", None, None, 0, 0, ctypes.c_float(1.0),
+                        ctypes.c_float(0.5), None, None) == mot.MOT_OK
