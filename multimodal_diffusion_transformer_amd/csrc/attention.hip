@@ -23,8 +23,10 @@
 //  * Online softmax in fp32 in the log2 domain (scale*log2(e) folded into
 //    one FMA before exp2).  The O rescale is skipped when no lane's running
 //    maximum moved.
-//  * Tiles are classified exactly per wave: empty tiles are skipped, full
-//    tiles run unmasked, only partial tiles evaluate the mask predicate.
+//  * Both masks give every query a prefix of the keys, [0, key_end(i)).  A
+//    per-lane limit decides each pair with one compare, and the limits of a
+//    wave's first and last rows classify its tiles exactly: empty tiles are
+//    skipped, full tiles run unmasked, only partial tiles are masked.
 //  * Grid: head is the fastest index, so with H a multiple of 8 every head
 //    stays on one XCD (workgroups go round-robin over the 8 XCDs) and shares
 //    that XCD's L2; query tiles are issued heaviest first.
@@ -261,6 +263,12 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
   const bool wave_live = rw < nq;
   const int64_t ia_w = p.m.q0 + rw;
   const int64_t ib_w = p.m.q0 + (rw + 31 < nq ? rw + 31 : nq - 1);
+  // Both masks allow each query a prefix of the keys, [0, key_end(i)), and
+  // key_end is non-decreasing in i: a per-lane limit decides every pair and
+  // the wave's first and last rows bound its tiles.
+  const int64_t lim = key_end(p.m, i_abs, i_abs);
+  const int64_t lim_lo = key_end(p.m, ia_w, ia_w);
+  const int64_t lim_hi = key_end(p.m, ib_w, ib_w);
 
   f32x16_t oacc[DT];
 #pragma unroll
@@ -284,11 +292,11 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
 
     const bf16_t* ks = smem + buf * S::STAGE;
     const bf16_t* vs = ks + S::K_ELEMS;
+    // exact per-wave class from the wave's smallest / largest key limit
     int cls = TILE_EMPTY;
     if (wave_live) {
-      int64_t jb = kbase + BN - 1 < p.m.nk ? kbase + BN - 1 : p.m.nk - 1;
-      cls = tile_class(p.m, ia_w, ib_w, kbase, jb);
-      if (cls == TILE_FULL && kbase + BN > p.m.nk) cls = TILE_PARTIAL;
+      if (kbase + BN <= lim_lo) cls = TILE_FULL;
+      else if (kbase < lim_hi) cls = TILE_PARTIAL;
     }
     if (cls != TILE_EMPTY) {
       // ---- S^T = K Q^T for two 32-key blocks ----
@@ -304,15 +312,15 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
           sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[st], 0, 0, 0);
         }
       }
-      // ---- mask (partial tiles only) ----
+      // ---- mask (partial tiles only): key j is allowed iff j < lim ----
       if (cls == TILE_PARTIAL) {
+        const int64_t rel = lim - kbase;
+        const int lrel = rel < 0 ? 0 : (rel > BN ? BN : (int)rel);
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int64_t j = kbase + 32 * st + 16 * g + r;
-            if (!(j < p.m.nk && mask_allowed(p.m, i_abs, j))) sacc[st][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * st + 16 * g + r >= lrel) sacc[st][r] = -INFINITY;
       }
       // ---- online softmax ----
       float mx = sacc[0][0];
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
       const float m_new = fmaxf(m_run, mx * p.c_log2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < DT; ++i)
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
         float pv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          pv[r] = exp2f(__builtin_fmaf(sacc[st][r], p.c_log2, -m_use));
+          pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][r], p.c_log2, -m_use));
           l_run += pv[r];
         }
 #pragma unroll
