@@ -4,7 +4,7 @@
 // attention of "Cosmos 3 方法原理全解" §3 (AR causal, DM full over [K_AR;K_DM])
 // and the chunk-causal streaming attention of "流式生成如何工作".
 //
-// Design (one workgroup = 4 waves = 128 query rows of one head):
+// Design (one workgroup = WAVES waves x 32 query rows of one head):
 //  * The score tile is computed transposed, S^T = K Q^T, on
 //    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane owns
 //    one column, so every lane owns ONE query and 16 of its keys; the row
@@ -14,15 +14,20 @@
 //    ends up holding keys 16g..16g+15 of each 32-key block in register
 //    order.  Those registers, packed to bf16, are exactly the B operand of
 //    O^T += V^T P^T for 8 consecutive keys: P never leaves registers.
+//  * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4:
+//    no staging registers, no VALU), issued one tile ahead into the other
+//    of two LDS stages.  Both are stored row-major with their 16-byte chunks
+//    XOR-swizzled per row.  K is read as the A operand with ds_read_b128;
+//    V^T is read with ds_read_b64_tr_b16, the gfx950 transposing LDS read
+//    (lane i of a 16-lane group gets 4 consecutive keys of one column).  The
+//    swizzles make both reads bank-conflict free.  All LDS addresses are
+//    loop-invariant per lane; tile bases are scalar.
 //  * Q (rotated by mRoPE on load when positions are given) lives in
-//    registers for the whole key loop.  K tiles sit in LDS row-major with a
-//    16-byte row pad; V tiles are transposed while staged (V^T[d][key]) with
-//    an XOR swizzle of 16-byte chunks, so both MFMA A-operand reads are
-//    conflict-free ds_read_b128.  Two LDS stages: the next tile's global
-//    loads are in flight while the current one is computed.
+//    registers for the whole key loop.
 //  * Online softmax in fp32 in the log2 domain (scale*log2(e) folded into
-//    one FMA before exp2).  The O rescale is skipped when no lane's running
-//    maximum moved.
+//    one FMA before exp2).  The reference maximum is only moved when a row's
+//    maximum grows by more than 2^8, so the O rescale almost never runs;
+//    the result is exact (the same reference scales numerator and sum).
 //  * Both masks give every query a prefix of the keys, [0, key_end(i)).  A
 //    per-lane limit decides each pair with one compare, and the limits of a
 //    wave's first and last rows classify its tiles exactly: empty tiles are
@@ -36,7 +41,11 @@
 namespace mot {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 struct AttnParams {
   const bf16_t* q;
@@ -54,18 +63,28 @@ struct AttnParams {
   RopeTable rope;
 };
 
-constexpr int BM = 128;  // query rows per workgroup
-constexpr int BN = 64;   // keys per tile
-constexpr int WAVES = 4;
+constexpr int BN = 64;             // keys per tile
+constexpr float RESCALE_TH = 8.f;  // log2 headroom before the reference max moves
+#ifndef MOT_ATTN_WAVES
+#define MOT_ATTN_WAVES 4
+#endif
+constexpr int ATTN_WAVES = MOT_ATTN_WAVES;
 
 template <int D>
-struct AttnSmem {
-  static constexpr int KROW = D + 8;                 // padded K row (elements)
-  static constexpr int K_ELEMS = BN * KROW;          // one stage
-  static constexpr int V_ELEMS = D * BN;             // one stage (V^T)
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * STAGE * 2;
+struct Lay {
+  static constexpr int CH = D / 8;            // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;          // bytes per row
+  static constexpr int TILE_B = BN * ROWB;    // one K or V tile
+  static constexpr int STAGE_B = 2 * TILE_B;  // K + V
+  static constexpr int BYTES = 2 * STAGE_B;   // two stages
+  static constexpr int RPG = 16 / CH;         // rows per 256-byte bank cycle
+  static constexpr int RPI = 64 / CH;         // rows per wave-wide 1 KB load
+  static constexpr int NINSTR = BN / RPI;     // 1 KB loads per tile
 };
+
+// Chunk swizzles: logical 16-byte chunk c of row r lives at chunk c ^ f(r).
+template <int D> __device__ inline int swz_k(int r) { return (r / Lay<D>::RPG) % Lay<D>::CH; }
+template <int D> __device__ inline int swz_v(int r) { return 4 * ((r / Lay<D>::RPG) % (Lay<D>::CH / 4)); }
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -79,131 +98,80 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 // 16g..16g+15 in accumulator registers 0..15.
 __device__ inline int key_perm(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
 
-// Physical 16-byte chunk of logical chunk ck in row d of the V^T tile.
-__device__ inline int v_swz(int d, int ck) { return ck ^ ((d >> 1) & 7); }
+template <int D, int W>
+struct TileLoader {
+  static constexpr int PER_WAVE = Lay<D>::NINSTR / W;
+  static_assert(PER_WAVE >= 1 && Lay<D>::NINSTR % W == 0, "loads per wave");
+  uint32_t offk[PER_WAVE], offv[PER_WAVE];  // byte offsets of this lane's chunk
+  int rowk[PER_WAVE];                       // tile row this lane loads
+  int ck[PER_WAVE], cv[PER_WAVE];           // logical chunks
 
-template <int D, bool ROPE_K>
-__device__ inline void load_kv_regs(const AttnParams& p, int head, int64_t kbase, uint4 (&kr)[4],
-                                    uint4 (&vr)[4]) {
-  const int t = threadIdx.x;
-  constexpr int CH = D / 8;  // 16-byte chunks per row
-  // K: thread -> (row, chunk c and c + CH/2); rows per pass = 256 / (CH/2)
-  constexpr int HALF = CH / 2;
-  constexpr int RPP = 256 / HALF;
-  constexpr int KPASS = BN / RPP;
-  static_assert(KPASS * 2 <= 4, "K staging registers");
+  __device__ void init(int wave, int lane, int64_t k_ts, int64_t v_ts) {
 #pragma unroll
-  for (int a = 0; a < KPASS; ++a) {
-    int row = t / HALF + a * RPP;
-    int c = t % HALF;
-    int64_t key = kbase + row;
-    if (key < p.m.nk) {
-      const bf16_t* src = p.k + key * p.k_ts + (int64_t)head * p.k_hs;
-      kr[2 * a] = *reinterpret_cast<const uint4*>(src + 8 * c);
-      kr[2 * a + 1] = *reinterpret_cast<const uint4*>(src + 8 * (c + HALF));
-    } else {
-      kr[2 * a] = make_uint4(0, 0, 0, 0);
-      kr[2 * a + 1] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int n = wave * PER_WAVE + i;
+      const int row = n * Lay<D>::RPI + lane / Lay<D>::CH;
+      const int pc = lane % Lay<D>::CH;
+      rowk[i] = row;
+      ck[i] = pc ^ swz_k<D>(row);
+      cv[i] = pc ^ swz_v<D>(row);
+      offk[i] = (uint32_t)(row * k_ts * 2 + ck[i] * 16);
+      offv[i] = (uint32_t)(row * v_ts * 2 + cv[i] * 16);
     }
   }
-  // V: thread -> (key block kb of 4 keys, d chunk db); D=128: 16 x 16.
-  constexpr int KB = BN / 4;
-  const int kb = t % KB;
-  const int db = t / KB;
-  if (db < CH) {
+
+  // Issue this wave's share of the K and V tile starting at key kbase into
+  // the LDS stage at `stage`.  Rows past the last key re-read the last key
+  // (never out of range; those scores are masked and the values finite).
+  __device__ void issue(const AttnParams& p, int head, int64_t kbase, unsigned char* stage,
+                        int wave) const {
+    const char* kb = reinterpret_cast<const char*>(p.k) + (kbase * p.k_ts + (int64_t)head * p.k_hs) * 2;
+    const char* vb = reinterpret_cast<const char*>(p.v) + (kbase * p.v_ts + (int64_t)head * p.v_hs) * 2;
+    const int64_t last = p.m.nk - 1 - kbase;  // last valid tile row
+    const bool ragged = last < BN - 1;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      int64_t key = kbase + 4 * kb + a;
-      if (key < p.m.nk) {
-        const bf16_t* src = p.v + key * p.v_ts + (int64_t)head * p.v_hs;
-        vr[a] = *reinterpret_cast<const uint4*>(src + 8 * db);
-      } else {
-        vr[a] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int n = wave * PER_WAVE + i;
+      uint32_t ok_ = offk[i], ov_ = offv[i];
+      if (ragged && rowk[i] > last) {
+        ok_ = (uint32_t)(last * p.k_ts * 2 + ck[i] * 16);
+        ov_ = (uint32_t)(last * p.v_ts * 2 + cv[i] * 16);
       }
+      __builtin_amdgcn_global_load_lds(kb + ok_, (lds_void_t*)(stage + n * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + ov_, (lds_void_t*)(stage + Lay<D>::TILE_B + n * 1024), 16, 0, 0);
     }
+  }
+};
+
+// Rotate the K tile in LDS by mRoPE (the optional rotate-on-load path).
+template <int D, int W>
+__device__ void rope_k_tile(const AttnParams& p, int64_t kbase, unsigned char* stage) {
+  constexpr int P = D / 2;
+  for (int e = threadIdx.x; e < BN * P; e += 64 * W) {
+    const int row = e / P, k = e % P;
+    const int64_t key = kbase + row;
+    if (key >= p.m.nk) continue;
+    float cs, sn;
+    rope_cs(p.k_pos[3 * key + rope_axis(p.rope, k)], p.rope.inv_freq[k], cs, sn);
+    const int f = swz_k<D>(row);
+    bf16_t* a = reinterpret_cast<bf16_t*>(stage + row * Lay<D>::ROWB + (((k / 8) ^ f) * 16) + (k % 8) * 2);
+    bf16_t* b = reinterpret_cast<bf16_t*>(stage + row * Lay<D>::ROWB + ((((k + P) / 8) ^ f) * 16) + (k % 8) * 2);
+    const float x1 = bf16_to_f32(*a), x2 = bf16_to_f32(*b);
+    *a = f32_to_bf16(__builtin_fmaf(x1, cs, -x2 * sn));
+    *b = f32_to_bf16(__builtin_fmaf(x1, sn, x2 * cs));
   }
 }
 
-template <int D, bool ROPE_K>
-__device__ inline void store_kv_lds(const AttnParams& p, int64_t kbase, bf16_t* ks, bf16_t* vs,
-                                    uint4 (&kr)[4], uint4 (&vr)[4]) {
-  using S = AttnSmem<D>;
-  const int t = threadIdx.x;
-  constexpr int CH = D / 8;
-  constexpr int HALF = CH / 2;
-  constexpr int RPP = 256 / HALF;
-  constexpr int KPASS = BN / RPP;
-#pragma unroll
-  for (int a = 0; a < KPASS; ++a) {
-    int row = t / HALF + a * RPP;
-    int c = t % HALF;
-    uint4 lo = kr[2 * a], hi = kr[2 * a + 1];
-    if (ROPE_K) {
-      int64_t key = kbase + row;
-      if (key < p.m.nk) {
-        const float* pp = p.k_pos + 3 * key;
-        uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w}, hw[4] = {hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          int kk = 8 * c + e;
-          float cs, sn;
-          rope_cs(pp[rope_axis(p.rope, kk)], p.rope.inv_freq[kk], cs, sn);
-          float x1 = bf16_to_f32((bf16_t)((e & 1) ? (lw[e >> 1] >> 16) : (lw[e >> 1] & 0xFFFF)));
-          float x2 = bf16_to_f32((bf16_t)((e & 1) ? (hw[e >> 1] >> 16) : (hw[e >> 1] & 0xFFFF)));
-          uint32_t y1 = f32_to_bf16(__builtin_fmaf(x1, cs, -x2 * sn));
-          uint32_t y2 = f32_to_bf16(__builtin_fmaf(x1, sn, x2 * cs));
-          if (e & 1) {
-            lw[e >> 1] = (lw[e >> 1] & 0xFFFFu) | (y1 << 16);
-            hw[e >> 1] = (hw[e >> 1] & 0xFFFFu) | (y2 << 16);
-          } else {
-            lw[e >> 1] = (lw[e >> 1] & 0xFFFF0000u) | y1;
-            hw[e >> 1] = (hw[e >> 1] & 0xFFFF0000u) | y2;
-          }
-        }
-        lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        hi = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      }
-    }
-    *reinterpret_cast<uint4*>(ks + row * S::KROW + 8 * c) = lo;
-    *reinterpret_cast<uint4*>(ks + row * S::KROW + 8 * (c + HALF)) = hi;
-  }
-  constexpr int KB = BN / 4;
-  const int kb = t % KB;
-  const int db = t / KB;
-  if (db < CH) {
-    // transpose 4 keys x 8 dims into 8 rows of V^T, 4 keys (8 bytes) each
-    uint32_t w[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      w[a][0] = vr[a].x; w[a][1] = vr[a].y; w[a][2] = vr[a].z; w[a][3] = vr[a].w;
-    }
-    const int ck = kb >> 1;   // logical 16-byte chunk (8 keys)
-    const int half = kb & 1;  // which 8-byte half of it
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int cw = e >> 1;
-      uint32_t k01, k23;
-      if (e & 1) {  // high halves
-        k01 = __builtin_amdgcn_perm(w[1][cw], w[0][cw], 0x07060302u);
-        k23 = __builtin_amdgcn_perm(w[3][cw], w[2][cw], 0x07060302u);
-      } else {      // low halves
-        k01 = __builtin_amdgcn_perm(w[1][cw], w[0][cw], 0x05040100u);
-        k23 = __builtin_amdgcn_perm(w[3][cw], w[2][cw], 0x05040100u);
-      }
-      const int d = 8 * db + e;
-      bf16_t* dst = vs + d * BN + 8 * v_swz(d, ck) + 4 * half;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(k01, k23);
-    }
-  }
-}
+__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int D, bool ROPE_Q, bool ROPE_K>
-__global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
-  using S = AttnSmem<D>;
+template <int D, int W, bool ROPE_Q, bool ROPE_K>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_mfma(AttnParams p) {
+  using L = Lay<D>;
+  constexpr int BM = 32 * W;
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DT = D / 32;      // 32-wide output tiles over the head dim
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
+  extern __shared__ __align__(16) unsigned char smem[];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -218,7 +186,26 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
   const bool row_ok = my_row < nq;
   const int64_t i_abs = p.m.q0 + my_row;
 
-  // ---- Q into registers (B operand of S^T = K Q^T) ----
+  // ---- key range of this workgroup and of this wave ----
+  const int64_t ia_wg = p.m.q0 + r0;
+  const int64_t ib_wg = p.m.q0 + (r0 + BM - 1 < nq ? r0 + BM - 1 : nq - 1);
+  const int64_t kend = key_end(p.m, ia_wg, ib_wg);
+  const int ntiles = (int)((kend + BN - 1) / BN);
+  const bool wave_live = rw < nq;
+  const int64_t ia_w = p.m.q0 + rw;
+  const int64_t ib_w = p.m.q0 + (rw + 31 < nq ? rw + 31 : nq - 1);
+  // Both masks allow each query a prefix of the keys, [0, key_end(i)), and
+  // key_end is non-decreasing in i: a per-lane limit decides every pair and
+  // the wave's first and last rows bound its tiles.
+  const int64_t lim = key_end(p.m, i_abs, i_abs);
+  const int64_t lim_lo = key_end(p.m, ia_w, ia_w);
+  const int64_t lim_hi = key_end(p.m, ib_w, ib_w);
+
+  // ---- start the first tile's loads, then bring Q into registers ----
+  TileLoader<D, W> ld;
+  ld.init(wave, lane, p.k_ts, p.v_ts);
+  ld.issue(p, head, 0, smem, wave);
+
   bf16x8_t qreg[KSTEPS];
   {
     uint4 raw[KSTEPS];
@@ -255,43 +242,46 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
     for (int s = 0; s < KSTEPS; ++s) qreg[s] = as_bf16x8(raw[s]);
   }
 
-  // ---- key range of this workgroup and of this wave ----
-  const int64_t ia_wg = p.m.q0 + r0;
-  const int64_t ib_wg = p.m.q0 + (r0 + BM - 1 < nq ? r0 + BM - 1 : nq - 1);
-  const int64_t kend = key_end(p.m, ia_wg, ib_wg);
-  const int ntiles = (int)((kend + BN - 1) / BN);
-  const bool wave_live = rw < nq;
-  const int64_t ia_w = p.m.q0 + rw;
-  const int64_t ib_w = p.m.q0 + (rw + 31 < nq ? rw + 31 : nq - 1);
-  // Both masks allow each query a prefix of the keys, [0, key_end(i)), and
-  // key_end is non-decreasing in i: a per-lane limit decides every pair and
-  // the wave's first and last rows bound its tiles.
-  const int64_t lim = key_end(p.m, i_abs, i_abs);
-  const int64_t lim_lo = key_end(p.m, ia_w, ia_w);
-  const int64_t lim_hi = key_end(p.m, ib_w, ib_w);
+  // ---- loop-invariant LDS read offsets (bytes within a stage) ----
+  uint32_t kaddr[KSTEPS];
+  {
+    const int row = key_perm(l32);
+    const int f = swz_k<D>(row);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) kaddr[s] = row * L::ROWB + (((2 * s + g) ^ f) * 16);
+  }
+  uint32_t vaddr[DT];
+  {
+    const int j = lane & 15, q16 = (lane >> 4) & 1;
+    const int rowl = 16 * g + j / 4;  // + 32st + 8t + 4h, all multiples of 4
+    const int f = swz_v<D>(rowl);     // so the swizzle is the same for all of them
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int c = 4 * dt + 2 * q16 + (j & 3) / 2;
+      vaddr[dt] = L::TILE_B + rowl * L::ROWB + ((c ^ f) * 16) + 8 * (j & 1);
+    }
+  }
 
   f32x16_t oacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
-  float m_run = -INFINITY;  // running max, log2 domain
+  float m_ref = -INFINITY;  // reference maximum (log2 domain)
   float l_run = 0.f;        // this lane's partial row sum
 
-  uint4 kr[4], vr[4];
-  load_kv_regs<D, ROPE_K>(p, head, 0, kr, vr);
-  store_kv_lds<D, ROPE_K>(p, 0, smem, smem + S::K_ELEMS, kr, vr);
+  wait_vmem();
   __syncthreads();
 
-  const int krow = key_perm(l32);
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
+    unsigned char* cur = smem + (kt & 1) * L::STAGE_B;
     const int64_t kbase = (int64_t)kt * BN;
-    const bool more = kt + 1 < ntiles;
-    if (more) load_kv_regs<D, ROPE_K>(p, head, kbase + BN, kr, vr);
+    if (kt + 1 < ntiles) ld.issue(p, head, kbase + BN, smem + ((kt + 1) & 1) * L::STAGE_B, wave);
+    if (ROPE_K) {
+      rope_k_tile<D, W>(p, kbase, cur);
+      __syncthreads();
+    }
 
-    const bf16_t* ks = smem + buf * S::STAGE;
-    const bf16_t* vs = ks + S::K_ELEMS;
     // exact per-wave class from the wave's smallest / largest key limit
     int cls = TILE_EMPTY;
     if (wave_live) {
@@ -305,11 +295,10 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[st][r] = 0.f;
-        const bf16_t* krp = ks + (32 * st + krow) * S::KROW + 8 * g;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-          bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(krp + 16 * s));
-          sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[s], sacc[st], 0, 0, 0);
+          const uint4 kv = *reinterpret_cast<const uint4*>(cur + kaddr[s] + st * 32 * L::ROWB);
+          sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), qreg[s], sacc[st], 0, 0, 0);
         }
       }
       // ---- mask (partial tiles only): key j is allowed iff j < lim ----
@@ -322,27 +311,28 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
           for (int r = 0; r < 16; ++r)
             if (32 * st + 16 * g + r >= lrel) sacc[st][r] = -INFINITY;
       }
-      // ---- online softmax ----
-      float mx = sacc[0][0];
+      // ---- online softmax with a lazily moved reference maximum ----
+      float mx = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[st][r]);
       {
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.c_log2;
       }
-      const float m_new = fmaxf(m_run, mx * p.c_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      const bool move = mx > m_ref + RESCALE_TH;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        const float m_new = move ? mx : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int i = 0; i < DT; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        m_ref = m_new;
       }
-      m_run = m_new;
+      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
       bf16x8_t pb[2][2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -359,25 +349,22 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
           pb[st][t] = as_bf16x8(u);
         }
       }
-      // ---- O^T += V^T P^T ----
+      // ---- O^T += V^T P^T; V^T comes from transposing LDS reads ----
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 32 * dt + l32;
-        const bf16_t* vrow = vs + d * BN;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const int ck = 4 * st + 2 * g + t;
-            bf16x8_t a = as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 8 * v_swz(d, ck)));
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[st][t], oacc[dt], 0, 0, 0);
+            unsigned char* base = cur + vaddr[dt] + (32 * st + 8 * t) * L::ROWB;
+            s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base));
+            s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + 4 * L::ROWB));
+            s16x8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8),
+                                                               pb[st][t], oacc[dt], 0, 0, 0);
           }
-      }
     }
-    if (more) {
-      bf16_t* nks = smem + (buf ^ 1) * S::STAGE;
-      store_kv_lds<D, ROPE_K>(p, kbase + BN, nks, nks + S::K_ELEMS, kr, vr);
-    }
+    wait_vmem();
     __syncthreads();
   }
 
@@ -399,22 +386,23 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnParams p) {
         w.y = pack_bf16(oacc[dt][4 * rr + 2] * inv_l, oacc[dt][4 * rr + 3] * inv_l);
         *reinterpret_cast<uint2*>(dst + d0) = w;
       }
-    if (p.lse && g == 0) p.lse[(int64_t)head * nq + my_row] = (m_run + log2f(l_run)) * 0.69314718055994530942f;
+    if (p.lse && g == 0) p.lse[(int64_t)head * nq + my_row] = (m_ref + log2f(l_run)) * 0.69314718055994530942f;
   }
 }
 
 template <int D, bool RQ, bool RK>
 static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
-  using S = AttnSmem<D>;
+  using L = Lay<D>;
+  constexpr int W = ATTN_WAVES;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_mfma<D, RQ, RK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_mfma<D, W, RQ, RK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
     if (e != hipSuccess) return e;
     configured = true;
   }
   dim3 grid((unsigned)(p.n_qtiles * p.n_heads));
-  hipLaunchKernelGGL((attn_fwd_mfma<D, RQ, RK>), grid, dim3(256), S::BYTES, s, p);
+  hipLaunchKernelGGL((attn_fwd_mfma<D, W, RQ, RK>), grid, dim3(64 * W), L::BYTES, s, p);
   return hipGetLastError();
 }
 
@@ -430,7 +418,7 @@ hipError_t attention_bf16_mfma(const mot_attn_args* a, const RopeTable& rt, hipS
   p.m.mode = a->mask; p.m.nq = a->nq; p.m.nk = a->nk; p.m.q0 = a->q0;
   p.m.n_ar = a->n_ar; p.m.n_prefix = a->n_prefix; p.m.chunk_len = a->chunk_len > 0 ? a->chunk_len : 1;
   p.n_heads = a->n_heads;
-  p.n_qtiles = (int)((a->nq + BM - 1) / BM);
+  p.n_qtiles = (int)((a->nq + 32 * ATTN_WAVES - 1) / (32 * ATTN_WAVES));
   float scale = a->scale != 0.f ? a->scale : 1.f / sqrtf((float)a->head_dim);
   p.c_log2 = scale * 1.4426950408889634f;
   p.q_pos = a->q_pos;
