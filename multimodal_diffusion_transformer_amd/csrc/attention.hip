@@ -15,8 +15,11 @@
 //    order.  Those registers, packed to bf16, are exactly the B operand of
 //    O^T += V^T P^T for 8 consecutive keys: P never leaves registers.
 //  * K and V tiles go from HBM straight into LDS (global_load_lds_dwordx4:
-//    no staging registers, no VALU), issued one tile ahead into the other
-//    of two LDS stages.  Both are stored row-major with their 16-byte chunks
+//    no staging registers, no VALU; vmcnt is managed explicitly so a tile's
+//    copy really overlaps the compute of the tiles before it), issued
+//    STAGES-1 tiles ahead into a
+//    ring of LDS stages, so the loads' latency hides behind that many tiles
+//    of compute.  Both are stored row-major with their 16-byte chunks
 //    XOR-swizzled per row.  K is read as the A operand with ds_read_b128;
 //    V^T is read with ds_read_b64_tr_b16, the gfx950 transposing LDS read
 //    (lane i of a 16-lane group gets 4 consecutive keys of one column).  The
@@ -68,7 +71,11 @@ constexpr float RESCALE_TH = 8.f;  // log2 headroom before the reference max mov
 #ifndef MOT_ATTN_WAVES
 #define MOT_ATTN_WAVES 4
 #endif
-constexpr int ATTN_WAVES = MOT_ATTN_WAVES;
+#ifndef MOT_ATTN_STAGES
+#define MOT_ATTN_STAGES 2
+#endif
+constexpr int ATTN_WAVES = MOT_ATTN_WAVES;    // waves per workgroup (32 query rows each)
+constexpr int ATTN_STAGES = MOT_ATTN_STAGES;  // LDS stages: tiles in flight = stages - 1
 
 template <int D>
 struct Lay {
@@ -76,17 +83,42 @@ struct Lay {
   static constexpr int ROWB = D * 2;          // bytes per row
   static constexpr int TILE_B = BN * ROWB;    // one K or V tile
   static constexpr int STAGE_B = 2 * TILE_B;  // K + V
-  static constexpr int BYTES = 2 * STAGE_B;   // two stages
   static constexpr int RPG = 16 / CH;         // rows per 256-byte bank cycle
   static constexpr int RPI = 64 / CH;         // rows per wave-wide 1 KB load
   static constexpr int NINSTR = BN / RPI;     // 1 KB loads per tile
 };
 
 // Chunk swizzles: logical 16-byte chunk c of row r lives at chunk c ^ f(r).
-template <int D> __device__ inline int swz_k(int r) { return (r / Lay<D>::RPG) % Lay<D>::CH; }
+// K rows are read by MFMA row rho = key_perm^-1 order, so one 8-lane group
+// touches rows {0..3, 16..19} (+4, +8, ...): the K swizzle gives those eight
+// rows eight different chunks (D=128: bits 0-1, 4, 2 of r; D=64: rows are
+// 128 B, so bit 0 picks the bank half and bits 1, 2, 4 the chunk).
+template <int D> __device__ inline int swz_k(int r) {
+  if constexpr (D == 128) return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 1) << 3);
+  else return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 4) & 1) << 2);
+}
 template <int D> __device__ inline int swz_v(int r) { return 4 * ((r / Lay<D>::RPG) % (Lay<D>::CH / 4)); }
 
 __device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// One wave-wide 16-byte-per-lane copy from global memory (scalar base +
+// per-lane offset) straight into LDS at `lds` + 16 * lane.  Written as
+// inline asm so the compiler does not drain every outstanding copy before
+// each LDS read (it cannot tell that the copies target another stage); the
+// kernel waits on vmcnt itself.  The instruction has no VGPR result.
+__device__ inline void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  // the tile base is wave-uniform by construction; make it an SGPR pair
+  const uint64_t b = (uint64_t)gbase;
+  // (readfirstlane returns int: go through uint32_t so nothing sign-extends)
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "{m0}"(lds) : "memory");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
 
 __device__ inline uint32_t pack_bf16(float a, float b) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
@@ -137,8 +169,8 @@ struct TileLoader {
         ok_ = (uint32_t)(last * p.k_ts * 2 + ck[i] * 16);
         ov_ = (uint32_t)(last * p.v_ts * 2 + cv[i] * 16);
       }
-      __builtin_amdgcn_global_load_lds(kb + ok_, (lds_void_t*)(stage + n * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + ov_, (lds_void_t*)(stage + Lay<D>::TILE_B + n * 1024), 16, 0, 0);
+      dma16(kb, ok_, lds_addr(stage + n * 1024));
+      dma16(vb, ov_, lds_addr(stage + Lay<D>::TILE_B + n * 1024));
     }
   }
 };
@@ -162,12 +194,27 @@ __device__ void rope_k_tile(const AttnParams& p, int64_t kbase, unsigned char* s
   }
 }
 
-__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-template <int D, int W, bool ROPE_Q, bool ROPE_K>
+// Wait until at most `ahead` tiles' loads (L per tile) are still in flight.
+template <int L, int NS>
+__device__ inline void wait_tiles(int ahead) {
+  if constexpr (NS >= 4) {
+    if (ahead >= 2) { wait_vmem<2 * L>(); return; }
+  }
+  if constexpr (NS >= 3) {
+    if (ahead >= 1) { wait_vmem<L>(); return; }
+  }
+  wait_vmem<0>();
+}
+
+template <int D, int W, int NS, bool ROPE_Q, bool ROPE_K>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma(AttnParams p) {
   using L = Lay<D>;
+  static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  constexpr int LPT = 2 * TileLoader<D, W>::PER_WAVE;  // this wave's loads per tile
   constexpr int BM = 32 * W;
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
   constexpr int DT = D / 32;      // 32-wide output tiles over the head dim
@@ -201,10 +248,8 @@ void attn_fwd_mfma(AttnParams p) {
   const int64_t lim_lo = key_end(p.m, ia_w, ia_w);
   const int64_t lim_hi = key_end(p.m, ib_w, ib_w);
 
-  // ---- start the first tile's loads, then bring Q into registers ----
   TileLoader<D, W> ld;
   ld.init(wave, lane, p.k_ts, p.v_ts);
-  ld.issue(p, head, 0, smem, wave);
 
   bf16x8_t qreg[KSTEPS];
   {
@@ -240,6 +285,10 @@ void attn_fwd_mfma(AttnParams p) {
     }
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) qreg[s] = as_bf16x8(raw[s]);
+    // Consume Q here so the compiler's own wait for these loads happens once,
+    // before the key loop, instead of at their first use inside it.
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) asm volatile("" ::"v"(qreg[s]));
   }
 
   // ---- loop-invariant LDS read offsets (bytes within a stage) ----
@@ -270,13 +319,20 @@ void attn_fwd_mfma(AttnParams p) {
   float m_ref = -INFINITY;  // reference maximum (log2 domain)
   float l_run = 0.f;        // this lane's partial row sum
 
-  wait_vmem();
+  // ---- prologue: NS-1 tiles in flight; wait for the first ----
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) ld.issue(p, head, (int64_t)t * BN, smem + t * L::STAGE_B, wave);
+  wait_tiles<LPT, NS>((ntiles < NS - 1 ? ntiles : NS - 1) - 1);
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    unsigned char* cur = smem + (kt & 1) * L::STAGE_B;
+    unsigned char* cur = smem + (kt % NS) * L::STAGE_B;
     const int64_t kbase = (int64_t)kt * BN;
-    if (kt + 1 < ntiles) ld.issue(p, head, kbase + BN, smem + ((kt + 1) & 1) * L::STAGE_B, wave);
+    {
+      const int nt = kt + NS - 1;  // the tile that reuses the stage freed last
+      if (nt < ntiles) ld.issue(p, head, (int64_t)nt * BN, smem + (nt % NS) * L::STAGE_B, wave);
+    }
     if (ROPE_K) {
       rope_k_tile<D, W>(p, kbase, cur);
       __syncthreads();
@@ -364,7 +420,12 @@ void attn_fwd_mfma(AttnParams p) {
                                                                pb[st][t], oacc[dt], 0, 0, 0);
           }
     }
-    wait_vmem();
+    // tile kt+1 must have landed; later tiles may still be in flight
+    {
+      const int last_issued = (kt + NS - 1 < ntiles - 1) ? kt + NS - 1 : ntiles - 1;
+      const int ahead = last_issued - (kt + 1);
+      wait_tiles<LPT, NS>(ahead < 0 ? 0 : ahead);
+    }
     __syncthreads();
   }
 
@@ -392,17 +453,17 @@ void attn_fwd_mfma(AttnParams p) {
 
 template <int D, bool RQ, bool RK>
 static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
-  using L = Lay<D>;
-  constexpr int W = ATTN_WAVES;
+  constexpr int W = ATTN_WAVES, NS = ATTN_STAGES;
+  constexpr int BYTES = NS * Lay<D>::STAGE_B;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_mfma<D, W, RQ, RK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_mfma<D, W, NS, RQ, RK>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, BYTES);
     if (e != hipSuccess) return e;
     configured = true;
   }
   dim3 grid((unsigned)(p.n_qtiles * p.n_heads));
-  hipLaunchKernelGGL((attn_fwd_mfma<D, W, RQ, RK>), grid, dim3(64 * W), L::BYTES, s, p);
+  hipLaunchKernelGGL((attn_fwd_mfma<D, W, NS, RQ, RK>), grid, dim3(64 * W), BYTES, s, p);
   return hipGetLastError();
 }
 
