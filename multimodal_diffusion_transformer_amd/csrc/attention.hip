@@ -28,9 +28,10 @@
 //  * Q (rotated by mRoPE on load when positions are given) lives in
 //    registers for the whole key loop.
 //  * Online softmax in fp32 in the log2 domain (scale*log2(e) folded into
-//    one FMA before exp2).  The reference maximum is only moved when a row's
-//    maximum grows by more than 2^8, so the O rescale almost never runs;
-//    the result is exact (the same reference scales numerator and sum).
+//    one FMA before exp2), against a reference maximum that only moves when
+//    a lane's tile sum exceeds 2^16: the common tile needs no max, no
+//    cross-lane step and no rescale.  Row sums are accumulated from the
+//    bf16-packed P with dot2, so numerator and denominator use the same P.
 //  * Both masks give every query a prefix of the keys, [0, key_end(i)).  A
 //    per-lane limit decides each pair with one compare, and the limits of a
 //    wave's first and last rows classify its tiles exactly: empty tiles are
@@ -47,6 +48,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -67,7 +69,7 @@ struct AttnParams {
 };
 
 constexpr int BN = 64;             // keys per tile
-constexpr float RESCALE_TH = 8.f;  // log2 headroom before the reference max moves
+constexpr float RESCALE_SUM = 65536.f;  // a lane's tile sum above this moves the reference max
 #ifndef MOT_ATTN_WAVES
 #define MOT_ATTN_WAVES 4
 #endif
@@ -213,7 +215,10 @@ template <int D, int W, int NS, bool ROPE_Q, bool ROPE_K>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma(AttnParams p) {
   using L = Lay<D>;
-  static_assert(NS >= 2 && NS <= 4, "LDS stages");
+  // Two stages only: every LDS destination of the tile copies stays below
+  // 64 KB.  A timing variant with four stages (128 KB) faulted the GPU once
+  // with no cause found in this code, so deeper rings are not built.
+  static_assert(NS == 2, "LDS stages");
   constexpr int LPT = 2 * TileLoader<D, W>::PER_WAVE;  // this wave's loads per tile
   constexpr int BM = 32 * W;
   constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
@@ -316,6 +321,7 @@ void attn_fwd_mfma(AttnParams p) {
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
   float m_ref = -INFINITY;  // reference maximum (log2 domain)
   float l_run = 0.f;        // this lane's partial row sum
 
@@ -367,44 +373,59 @@ void attn_fwd_mfma(AttnParams p) {
           for (int r = 0; r < 16; ++r)
             if (32 * st + 16 * g + r >= lrel) sacc[st][r] = -INFINITY;
       }
-      // ---- online softmax with a lazily moved reference maximum ----
-      float mx = fmaxf(sacc[0][0], sacc[0][1]);
+      // ---- online softmax against a lazily moved reference maximum ----
+      // Fast path: P = exp2(s*c - m_ref) with the current reference, packed
+      // to bf16; the row sum accumulates those bf16 values with dot2 (the
+      // same numbers the PV product uses).  Only when some lane's tile sum
+      // exceeds 2^16 (or is not finite: first tile, m_ref = -inf) does the
+      // wave compute the tile maximum, move the reference, rescale O and
+      // redo the exponentials.  Exact either way: numerator and sum always
+      // share one reference.
+      bf16x8_t pb[2][2];
+      float l_tile = 0.f;
+      auto exps = [&](float m_use) {
+        l_tile = 0.f;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[st][r]);
-      {
+          for (int t = 0; t < 2; ++t) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][8 * t + 2 * e], p.c_log2, -m_use));
+              const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][8 * t + 2 * e + 1], p.c_log2, -m_use));
+              w[e] = pack_bf16(a, b);
+              l_tile = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones2, l_tile, false);
+            }
+            pb[st][t] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+          }
+      };
+      bool slow = __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) != 0;  // a row's first tile
+      if (!slow) {
+        exps(m_ref);
+        slow = __builtin_amdgcn_ballot_w64(!(l_tile <= RESCALE_SUM)) != 0;
+      }
+      if (slow) {
+        float mx = fmaxf(sacc[0][0], sacc[0][1]);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[st][r]);
         auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
         mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * p.c_log2;
-      }
-      const bool move = mx > m_ref + RESCALE_TH;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        const float m_new = move ? mx : m_ref;
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-        l_run *= alpha;
+        const float m_new = fmaxf(m_ref, mx);
+        if (m_new > m_ref) {  // per lane: only rows whose reference moves
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+          l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < DT; ++i)
+          for (int i = 0; i < DT; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-        m_ref = m_new;
-      }
-      const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-      bf16x8_t pb[2][2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        float pv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[st][r], p.c_log2, -m_use));
-          l_run += pv[r];
+            for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+          m_ref = m_new;
         }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          uint4 u = make_uint4(pack_bf16(pv[8 * t + 0], pv[8 * t + 1]), pack_bf16(pv[8 * t + 2], pv[8 * t + 3]),
-                               pack_bf16(pv[8 * t + 4], pv[8 * t + 5]), pack_bf16(pv[8 * t + 6], pv[8 * t + 7]));
-          pb[st][t] = as_bf16x8(u);
-        }
+        exps(m_ref == -INFINITY ? 0.f : m_ref);
       }
+      l_run += l_tile;
       // ---- O^T += V^T P^T; V^T comes from transposing LDS reads ----
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
