@@ -26,6 +26,41 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+ATTN_KERNEL = "attn_fwd_mfma"
+# sources whose text decides the attention kernel's memory traffic
+ATTN_SOURCES = ("multimodal_diffusion_transformer_amd/csrc/attention.hip",
+                "multimodal_diffusion_transformer_amd/csrc/common.hpp",
+                "multimodal_diffusion_transformer_amd/csrc/rope_dev.hpp")
+
+
+def attention_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per attention launch as recorded in profiles/ by the two
+    counter runs (FETCH_SIZE, WRITE_SIZE) and their copy calibration, or None
+    when the attention sources changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.txt" % (ATTN_KERNEL, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("attention_source_hash") != attention_source_hash():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def attention_pairs(n, n_ar):
@@ -35,10 +70,11 @@ def attention_pairs(n, n_ar):
 
 
 def cpu_baseline(wl, budget_s=15.0):
-    """Time the fp64 oracle attention on a bounded sample: one head, blocks
-    of DM query rows (each reading all keys) until ~budget_s of CPU work."""
+    """Time the fp64 oracle attention on a bounded sample: blocks of 256 DM
+    query rows (each reading all keys) of one head after another, until about
+    budget_s of CPU work; reports the BLAS threads the oracle actually used."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import workloads as W
     from oracle import attention as oattn
@@ -46,25 +82,28 @@ def cpu_baseline(wl, budget_s=15.0):
     n = wl.n_tokens
     n_ar = W.region_counts(wl.segments)[0]
     d = wl.head_dim
-    cores = len(os.sched_getaffinity(0))
+    avail = len(os.sched_getaffinity(0))
     rng = np.random.default_rng(0)
-    q = rng.standard_normal((n, 1, d)).astype(np.float32)
-    k = rng.standard_normal((n, 1, d)).astype(np.float32)
-    v = rng.standard_normal((n, 1, d)).astype(np.float32)
-    rows_done = 0
+    rows_done = heads = 0
     flops = 0.0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=cores):
-        while time.perf_counter() - t0 < budget_s and rows_done < n - n_ar:
-            r0 = n_ar + rows_done
-            r1 = min(n, r0 + 256)
-            oattn.attention(q[r0:r1], k, v, r0, W.AR_CAUSAL_DM_FULL, n_ar=n_ar)
-            flops += oattn.flops((r1 - r0) * n, 1, d)
-            rows_done += r1 - r0
+    with threadpool_limits(limits=avail):
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        while time.perf_counter() - t0 < budget_s and heads < wl.n_heads:
+            q, k, v = (rng.standard_normal((n, 1, d)).astype(np.float32) for _ in range(3))
+            heads += 1
+            r0 = n_ar
+            while r0 < n and time.perf_counter() - t0 < budget_s:
+                r1 = min(n, r0 + 256)
+                oattn.attention(q[r0:r1], k, v, r0, W.AR_CAUSAL_DM_FULL, n_ar=n_ar)
+                flops += oattn.flops((r1 - r0) * n, 1, d)
+                rows_done += r1 - r0
+                r0 = r1
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": "fp64 oracle attention, 1 of %d heads, %d DM query rows x %d keys "
-                      "(%.1f s wall)" % (wl.n_heads, rows_done, n, dt)}
+            "sample": "fp64 oracle attention over %d DM query rows x %d keys (%d of %d heads "
+                      "started, one head at a time), %.1f s wall" % (rows_done, n, heads,
+                                                                   wl.n_heads, dt)}
 
 
 def main():
@@ -75,7 +114,15 @@ def main():
     ap.add_argument("--workload", default="t2v480p_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (10 times), the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--rocprof-summary", metavar="DIR",
+                    help="only summarise rocprofv3 CSV output under DIR (no GPU use)")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the multi-GPU path (head-sharded attention "
               "behind an all-to-all) is a design, not built; run with --gpus 1", file=sys.stderr)
@@ -83,6 +130,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 10}), flush=True)
+        return
 
     import workloads as W
     from multimodal_diffusion_transformer_amd import pipeline
@@ -161,11 +218,43 @@ def main():
         "breakdown_ms": {k: round(v, 4) for k, v in per.items()},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_from_profile(wl.name)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)
+
+
+def rocprof_summary(d):
+    """Per-kernel summary of rocprofv3 CSV output: the --stats table, and the
+    per-dispatch mean of every collected counter (each counter's values are
+    summed over its dimension instances within a dispatch first)."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        out.append("kernel stats (%s):" % os.path.relpath(f, d))
+        out.append("  %-48s %6s %14s %12s %7s" % ("kernel", "calls", "total_ns", "avg_ns", "pct"))
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                out.append("  %-48s %6s %14s %12.0f %7.2f" % (
+                    row["Name"][:48], row["Calls"], row["TotalDurationNs"],
+                    float(row["AverageNs"]), float(row["Percentage"])))
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        per = defaultdict(lambda: defaultdict(float))  # (kernel, counter) -> dispatch -> value
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = row["Kernel_Name"].split("(")[0][-48:]
+                per[(name, row["Counter_Name"])][row["Dispatch_Id"]] += float(row["Counter_Value"])
+        out.append("counters (%s), mean per dispatch:" % os.path.relpath(f, d))
+        for (name, cname), disp in sorted(per.items()):
+            vals = list(disp.values())
+            out.append("  %-48s %-14s dispatches %4d  mean %.6g" % (name, cname, len(vals),
+                                                                  sum(vals) / len(vals)))
+    return "\n".join(out)
 
 
 if __name__ == "__main__":
