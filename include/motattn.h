@@ -164,7 +164,11 @@ typedef struct {
  * on MFMA with fp32 online softmax and skips tiles with no allowed pair;
  * fp32 runs on the vector ALUs in fp32.  Requires nq >= 1, nk >= q0 + nq in
  * AR mode (every query sees its diagonal), q0 >= n_prefix and chunk_len >= 1
- * in chunk mode, 0 <= n_ar, n_prefix <= nk. */
+ * in chunk mode, 0 <= n_ar, n_prefix <= nk.  bf16 returns
+ * MOT_ERR_UNSUPPORTED when k_pos is set (bf16 rotates Q on load only: rotate
+ * K beforehand with mrope_apply, which is also the layout a key cache keeps),
+ * when nk > 2^31 - 65 or nq > 2^31 - 1, or when a 64-row tile of K or V
+ * spans 4 GiB or more (128 * max(k_ts, v_ts) >= 2^32). */
 mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
 
 /* Flow-matching Euler update (method page §7.2), in place:

@@ -84,6 +84,13 @@ extern "C" mot_status mot_attention_fwd(const mot_attn_args* a, void* stream) {
   if (((uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v | (uintptr_t)a->o) & 15)
     return MOT_ERR_INVALID_ARG;
   if ((uintptr_t)a->lse & 3) return MOT_ERR_INVALID_ARG;
+  // the bf16 kernel keeps key indices in 32 bits and addresses a 64-key tile
+  // with 32-bit unsigned lane offsets from the tile base
+  if (a->dt == MOT_BF16 &&
+      (a->nk > INT32_MAX - 64 || a->nq > INT32_MAX || 64 * (a->k_ts > a->v_ts ? a->k_ts : a->v_ts) * 2 >= (1LL << 32)))
+    return MOT_ERR_UNSUPPORTED;
+  // the bf16 kernel rotates Q on load only; K is rotated beforehand (mrope_apply)
+  if (a->dt == MOT_BF16 && a->k_pos) return MOT_ERR_UNSUPPORTED;
   RopeTable rt;
   rt.sec_t = a->sec_t;
   rt.sec_th = a->sec_t + a->sec_h;

@@ -67,13 +67,12 @@ struct AttnParams {
   int n_qtiles;
   float c_log2;  // scale * log2(e)
   const float* q_pos;
-  const float* k_pos;
   RopeTable rope;
 };
 
 constexpr int BN = 64;                  // keys per tile
 constexpr int NST = BN / 32;            // 32-key MFMA blocks per tile
-constexpr float RESCALE_SUM = 65536.f;  // a lane's tile sum above this moves the reference max
+constexpr float OVERFLOW_SUM = 18446744073709551616.f;  // 2^64: a lane's tile sum above this moves the reference
 #ifndef MOT_ATTN_WAVES
 #define MOT_ATTN_WAVES 4
 #endif
@@ -96,26 +95,27 @@ struct Lay {
 // different chunks (D=128: bits 0-1, 4, 2 of r; D=64: rows are 128 B, so bit
 // 0 picks the bank half and bits 1, 2, 4 the chunk).  V is read four rows
 // at a time by 16-lane groups; its swizzle separates rows r%4.
-template <int D> __device__ inline int swz_k(int r) {
+template <int D> __device__ __forceinline__ int swz_k(int r) {
   if constexpr (D == 128) return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 1) << 3);
   else return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 4) & 1) << 2);
 }
-template <int D> __device__ inline int swz_v(int r) { return 4 * ((r / Lay<D>::RPG) % (Lay<D>::CH / 4)); }
+template <int D> __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / Lay<D>::RPG) % (Lay<D>::CH / 4)); }
 
-__device__ inline bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-__device__ inline uint32_t pack_bf16(float a, float b) {
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
   bf2 p = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, p);
 }
 
 // One wave-wide 16-byte-per-lane copy from global memory (scalar base +
-// per-lane offset) straight into LDS at `lds` + 16 * lane.  Written as
+// per-lane offset, which the hardware adds as an unsigned 32-bit value, so it
+// must never be "negative") straight into LDS at `lds` + 16 * lane.  Written as
 // inline asm so the compiler does not drain every outstanding copy before
 // each LDS read (it cannot tell that the copies target another stage); the
 // kernel waits on vmcnt itself.  The instruction has no VGPR result.
-__device__ inline void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   // the tile base is wave-uniform by construction; make it an SGPR pair
   // (readfirstlane returns int: go through uint32_t so nothing sign-extends)
   const uint64_t b = (uint64_t)gbase;
@@ -125,175 +125,308 @@ __device__ inline void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "{m0}"(lds) : "memory");
 }
 
-__device__ inline uint32_t lds_addr(const void* p) {
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-__device__ inline void wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Row of the K tile that feeds MFMA row rho so that lane half g holds keys
 // 16g..16g+15 in accumulator registers 0..15.
-__device__ inline int key_perm(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
+__device__ __forceinline__ int key_perm(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
 
 template <int D, int W>
 struct TileLoader {
   static constexpr int PER_WAVE = Lay<D>::NINSTR / W;
   static_assert(PER_WAVE >= 1 && Lay<D>::NINSTR % W == 0, "loads per wave");
-  uint32_t offk[PER_WAVE], offv[PER_WAVE];  // byte offsets of this lane's chunk
-  int row[PER_WAVE];                        // tile row this lane loads
-  int ck[PER_WAVE], cv[PER_WAVE];           // logical chunks
-  int wave;
+  // Load i of a wave copies tile row r = RPI (wave PER_WAVE + i) + lane / CH,
+  // and its chunk depends on r only through the swizzle.  With RPI = 64 / CH
+  // rows per load, the swizzle bits that vary with i are bit 2 of r at
+  // D = 128 (so only i & 1 matters) and none at D = 64, or for V: the lane
+  // part of the byte offset takes NVAR_K values over i for K and one for V.
+  static constexpr int NVAR_K = D == 128 ? 2 : 1;
+  uint32_t lk[NVAR_K], lv;  // lane parts of the byte offsets
+  uint32_t k_row_b, v_row_b;  // bytes per RPI rows (wave-uniform)
+  int wave;                   // wave-uniform
 
-  __device__ void init(int wave_, int lane, int64_t k_ts, int64_t v_ts) {
+  __device__ __forceinline__ static int row_of(int wave, int i, int lane) {
+    return (wave * PER_WAVE + i) * Lay<D>::RPI + lane / Lay<D>::CH;
+  }
+  template <bool IS_K>
+  __device__ __forceinline__ static int chunk_of(int r, int lane) {
+    return (lane % Lay<D>::CH) ^ (IS_K ? swz_k<D>(r) : swz_v<D>(r));
+  }
+
+  __device__ __forceinline__ void init(int wave_, int lane, int64_t k_ts, int64_t v_ts) {
     wave = wave_;
+    k_row_b = (uint32_t)(Lay<D>::RPI * k_ts * 2);
+    v_row_b = (uint32_t)(Lay<D>::RPI * v_ts * 2);
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int n = wave * PER_WAVE + i;
-      const int r = n * Lay<D>::RPI + lane / Lay<D>::CH;
-      const int pc = lane % Lay<D>::CH;
-      row[i] = r;
-      ck[i] = pc ^ swz_k<D>(r);
-      cv[i] = pc ^ swz_v<D>(r);
-      offk[i] = (uint32_t)(r * k_ts * 2 + ck[i] * 16);
-      offv[i] = (uint32_t)(r * v_ts * 2 + cv[i] * 16);
+    for (int i = 0; i < NVAR_K; ++i) {
+      const int r = row_of(wave, i, lane);
+      lk[i] = (uint32_t)((lane / Lay<D>::CH) * k_ts * 2 + chunk_of<true>(r, lane) * 16);
     }
+    lv = (uint32_t)((lane / Lay<D>::CH) * v_ts * 2 + chunk_of<false>(row_of(wave, 0, lane), lane) * 16);
   }
 
   // Issue this wave's share of one tile (K or V) starting at key kbase into
   // the LDS tile at `dst`.  Rows past the last key re-read the last key
   // (never out of range; those scores are masked and the values finite).
   template <bool IS_K>
-  __device__ void issue(const AttnParams& p, int head, int64_t kbase, unsigned char* dst) const {
+  __device__ __forceinline__ void issue(const AttnParams& p, int head, int64_t kbase, unsigned char* dst) const {
     const int64_t ts = IS_K ? p.k_ts : p.v_ts;
     const char* base = reinterpret_cast<const char*>(IS_K ? p.k : p.v) +
                        (kbase * ts + (int64_t)head * (IS_K ? p.k_hs : p.v_hs)) * 2;
     const int64_t last = p.m.nk - 1 - kbase;  // last valid tile row
-    const bool ragged = last < BN - 1;
+    if (__builtin_expect(last >= BN - 1, 1)) {
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int n = wave * PER_WAVE + i;
-      uint32_t off = IS_K ? offk[i] : offv[i];
-      if (ragged && row[i] > last) off = (uint32_t)(last * ts * 2 + (IS_K ? ck[i] : cv[i]) * 16);
-      dma16(base, off, lds_addr(dst + n * 1024));
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int n = wave * PER_WAVE + i;
+        const uint32_t rows_b = (uint32_t)n * (IS_K ? k_row_b : v_row_b);  // wave-uniform
+        dma16(base + rows_b, IS_K ? lk[i % NVAR_K] : lv, lds_addr(dst + n * 1024));
+      }
+    } else {  // the ragged last tile: full per-lane offsets from the tile base
+      const int lane = threadIdx.x & 63;
+#pragma unroll
+      for (int i = 0; i < PER_WAVE; ++i) {
+        const int n = wave * PER_WAVE + i;
+        const int r = row_of(wave, i, lane);
+        const int64_t rr = r > last ? last : r;  // never negative: the lane offset is unsigned
+        dma16(base, (uint32_t)(rr * ts * 2 + chunk_of<IS_K>(r, lane) * 16), lds_addr(dst + n * 1024));
+      }
     }
   }
 };
 
-// Rotate a K tile in LDS by mRoPE (the optional rotate-on-load path).
-template <int D, int W>
-__device__ void rope_k_tile(const AttnParams& p, int64_t kbase, unsigned char* tile) {
-  constexpr int P = D / 2;
-  for (int e = threadIdx.x; e < BN * P; e += 64 * W) {
-    const int row = e / P, k = e % P;
-    const int64_t key = kbase + row;
-    if (key >= p.m.nk) continue;
+// Rotate one row's chunk pair by mRoPE in registers: lo holds dims
+// 16s+8g..+7 and hi the dims D/2 above them, which are their rotate-half
+// partners.  pp points at the row's (t, h, w).
+template <int D>
+__device__ __forceinline__ void rope_chunk_pair(const RopeTable& rt, const float* pp, int s, int g, uint4& lo, uint4& hi) {
+  const uint32_t lw[4] = {lo.x, lo.y, lo.z, lo.w};
+  const uint32_t hw[4] = {hi.x, hi.y, hi.z, hi.w};
+  float y1[8], y2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int kk = 16 * s + 8 * g + e;
     float cs, sn;
-    rope_cs(p.k_pos[3 * key + rope_axis(p.rope, k)], p.rope.inv_freq[k], cs, sn);
-    const int f = swz_k<D>(row);
-    bf16_t* a = reinterpret_cast<bf16_t*>(tile + row * Lay<D>::ROWB + (((k / 8) ^ f) * 16) + (k % 8) * 2);
-    bf16_t* b = reinterpret_cast<bf16_t*>(tile + row * Lay<D>::ROWB + ((((k + P) / 8) ^ f) * 16) + (k % 8) * 2);
-    const float x1 = bf16_to_f32(*a), x2 = bf16_to_f32(*b);
-    *a = f32_to_bf16(__builtin_fmaf(x1, cs, -x2 * sn));
-    *b = f32_to_bf16(__builtin_fmaf(x1, sn, x2 * cs));
+    rope_cs(pp[rope_axis(rt, kk)], rt.inv_freq[kk], cs, sn);
+    const float x1 = __uint_as_float((e & 1) ? (lw[e >> 1] & 0xFFFF0000u) : (lw[e >> 1] << 16));
+    const float x2 = __uint_as_float((e & 1) ? (hw[e >> 1] & 0xFFFF0000u) : (hw[e >> 1] << 16));
+    y1[e] = __builtin_fmaf(x1, cs, -x2 * sn);
+    y2[e] = __builtin_fmaf(x1, sn, x2 * cs);
   }
+  lo = make_uint4(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]), pack_bf16(y1[4], y1[5]), pack_bf16(y1[6], y1[7]));
+  hi = make_uint4(pack_bf16(y2[0], y2[1]), pack_bf16(y2[2], y2[3]), pack_bf16(y2[4], y2[5]), pack_bf16(y2[6], y2[7]));
 }
 
 // Per-wave state of the key loop.
 template <int D>
 struct WaveState {
-  static constexpr int KSTEPS = D / 16;  // MFMA k-steps over the head dim
-  static constexpr int DT = D / 32;      // 32-wide output tiles over the head dim
-  bf16x8_t qreg[KSTEPS];
+  static constexpr int KSTEPS = D / 16;       // MFMA k-steps over the head dim
+  static constexpr int DT = D / 32;           // 32-wide output tiles over the head dim
+  static constexpr int NSM = NST * KSTEPS;    // score MFMAs per tile
+  static constexpr int NPV = NST * 2 * DT;    // PV MFMAs per tile
+  static_assert(NSM == NPV, "score and PV MFMAs alternate one to one");
+  bf16x8_t qreg[KSTEPS];   // B operand of S^T = K Q^T
   uint32_t kaddr[KSTEPS];  // K operand offsets within a K tile
   uint32_t vaddr[DT];      // V^T operand offsets within a V tile
   f32x16_t oacc[DT];
-  float m_ref;  // reference maximum (log2 domain)
+  float m_ref;  // reference maximum (log2 domain): P = exp2(S c - m_ref)
   float l_run;  // this lane's partial row sum
-  int64_t lim;  // this lane's key limit
+  int lim;      // this lane's key limit
 };
 
-// S^T = K Q^T for one tile (NST 32-key blocks).
+// A operand of score MFMA n: 32-key block n / KSTEPS, k-step n % KSTEPS.
 template <int D>
-__device__ inline void scores(const WaveState<D>& ws, const unsigned char* ktile, f32x16_t (&s)[NST]) {
-  using L = Lay<D>;
+__device__ __forceinline__ bf16x8_t k_operand(const WaveState<D>& ws, const unsigned char* ktile, int n) {
+  const int st = n / WaveState<D>::KSTEPS, s = n % WaveState<D>::KSTEPS;
+  return as_bf16x8(*reinterpret_cast<const uint4*>(ktile + ws.kaddr[s] + st * 32 * Lay<D>::ROWB));
+}
+
+// A operand (V^T, 32 dims x 8+8 keys) of PV MFMA n: key block n / (2 DT),
+// output tile n % DT, key half (n / DT) % 2.
+template <int D>
+__device__ __forceinline__ bf16x8_t v_operand(const WaveState<D>& ws, const unsigned char* vtile, int n) {
+  constexpr int DT = WaveState<D>::DT;
+  const int st = n / (2 * DT), dt = n % DT, t = (n / DT) % 2;
+  const unsigned char* base = vtile + ws.vaddr[dt] + (32 * st + 8 * t) * Lay<D>::ROWB;
+  s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base));
+  s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + 4 * Lay<D>::ROWB));
+  s16x8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8_t, a8);
+}
+
+// One step of the key loop, as a fixed instruction schedule.  It runs up to
+// three independent streams:
+//   DO_S : the score MFMAs of the next tile, nxt = K(j+1) Q^T;
+//   DO_PV: the PV MFMAs of the previous tile, O^T += V(j-1)^T P(j-1)^T;
+//   DO_E : the exponentials of this tile, P(j) = exp2(cur * c - m_ref)
+//          packed to bf16, and their lane sum (c = scale * log2(e)).
+// No stream depends on another inside a step, so the schedule alternates
+// score and PV MFMAs, spreads the VALU operations of the exponentials
+// evenly between them, and reads each MFMA's LDS operand PD MFMAs ahead.
+// A scheduling fence after every MFMA keeps that order.
+template <int D, bool DO_S, bool DO_E, bool DO_PV>
+__device__ __forceinline__ void tile_step(WaveState<D>& ws, const unsigned char* ktile,
+                                          const unsigned char* vtile, const f32x16_t (&cur)[NST],
+                                          f32x16_t (&nxt)[NST], const bf16x8_t (&pprev)[NST][2],
+                                          bf16x8_t (&pcur)[NST][2], float c, float& l_tile) {
+  using WS = WaveState<D>;
+  constexpr int NM = (DO_S ? WS::NSM : 0) + (DO_PV ? WS::NPV : 0);
+  constexpr int OPP = 6;  // per value pair: fma, fma, exp, exp, pack, dot2
+  constexpr int NOPS = DO_E ? OPP * NST * 8 : 0;
+  const f32x16_t zero16 = {};
+  constexpr int PD = 2, NB = PD + 1;
+  const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+  auto is_s = [](int m) { return DO_S && (!DO_PV || (m % 2 == 0)); };
+  auto idx = [](int m) { return (DO_S && DO_PV) ? m / 2 : m; };
+  bf16x8_t ops[NB];
 #pragma unroll
-  for (int st = 0; st < NST; ++st) {
+  for (int m = 0; m < PD && m < NM; ++m)
+    ops[m] = is_s(m) ? k_operand<D>(ws, ktile, idx(m)) : v_operand<D>(ws, vtile, idx(m));
+  float ex0 = 0.f, ex1 = 0.f;
+  uint32_t w[NST][2][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[st][r] = 0.f;
-#pragma unroll
-    for (int k = 0; k < WaveState<D>::KSTEPS; ++k) {
-      const uint4 kv = *reinterpret_cast<const uint4*>(ktile + ws.kaddr[k] + st * 32 * L::ROWB);
-      s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kv), ws.qreg[k], s[st], 0, 0, 0);
+  for (int m = 0; m < NM; ++m) {
+    if (m + PD < NM)
+      ops[(m + PD) % NB] = is_s(m + PD) ? k_operand<D>(ws, ktile, idx(m + PD))
+                                        : v_operand<D>(ws, vtile, idx(m + PD));
+    if (is_s(m)) {
+      const int n = idx(m), st = n / WS::KSTEPS, s = n % WS::KSTEPS;
+      nxt[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[m % NB], ws.qreg[s], s == 0 ? zero16 : nxt[st],
+                                                        0, 0, 0);
+    } else {
+      const int n = idx(m), st = n / (2 * WS::DT), dt = n % WS::DT, t = (n / WS::DT) % 2;
+      ws.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ops[m % NB], pprev[st][t], ws.oacc[dt], 0, 0, 0);
     }
+    if (DO_E) {
+#pragma unroll
+      for (int k = m * NOPS / NM; k < (m + 1) * NOPS / NM; ++k) {
+        const int pr = k / OPP, kind = k % OPP;
+        const int st = pr / 8, t = (pr % 8) / 4, e = pr % 4, r0 = 8 * t + 2 * e;
+        if (kind == 0) {
+          ex0 = __builtin_fmaf(cur[st][r0], c, -ws.m_ref);
+        } else if (kind == 1) {
+          ex1 = __builtin_fmaf(cur[st][r0 + 1], c, -ws.m_ref);
+        } else if (kind == 2) {
+          ex0 = __builtin_amdgcn_exp2f(ex0);
+        } else if (kind == 3) {
+          ex1 = __builtin_amdgcn_exp2f(ex1);
+        } else if (kind == 4) {
+          w[st][t][e] = pack_bf16(ex0, ex1);
+          if (e == 3) pcur[st][t] = as_bf16x8(make_uint4(w[st][t][0], w[st][t][1], w[st][t][2], w[st][t][3]));
+        } else {
+          l_tile = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[st][t][e]), ones2, l_tile, false);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// P = exp2(s*c - m) packed to bf16; returns the lane's sum of the packed P.
-__device__ inline float exps(const f32x16_t (&s)[NST], float c, float m_use, bf16x8_t (&pb)[NST][2]) {
-  const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
-  float l = 0.f;
+// Per-query max of a score tile (both lane halves), NaN-propagating.
+__device__ __forceinline__ float query_max(const f32x16_t (&sc)[NST]) {
+  float mx = sc[0][0];
 #pragma unroll
   for (int st = 0; st < NST; ++st)
+#pragma unroll
+    for (int r = (st == 0 ? 1 : 0); r < 16; r += 2)
+      mx = r + 1 < 16 ? __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[st][r]), sc[st][r + 1])
+                      : __builtin_elementwise_maximum(mx, sc[st][r]);
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Masks a score tile for keys at or past this lane's limit.
+__device__ __forceinline__ void mask_tile(f32x16_t (&sc)[NST], int lim, int kbase, int g) {
+  const int rel = lim - kbase - 16 * g;  // compared with compile-time key offsets
+#pragma unroll
+  for (int st = 0; st < NST; ++st)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * st + r >= rel) sc[st][r] = -INFINITY;
+}
+
+// Scores of one 32-key block of tile kbase, recomputed from K in global
+// memory, masked like the tile.
+template <int D>
+__device__ __forceinline__ f32x16_t block_scores(const AttnParams& p, const WaveState<D>& ws, int head, int kbase, int st,
+                                        bool partial, int lane) {
+  constexpr int KSTEPS = WaveState<D>::KSTEPS;
+  const int g = lane >> 5;
+  int64_t key = (int64_t)kbase + key_perm(lane & 31) + 32 * st;
+  if (key > p.m.nk - 1) key = p.m.nk - 1;  // masked below; any valid row will do
+  const bf16_t* row = p.k + key * p.k_ts + (int64_t)head * p.k_hs;
+  f32x16_t sc = {};
+  // two k-steps at a time (few registers; this path is rare): the fence
+  // keeps the loads from being hoisted together
+#pragma unroll
+  for (int s = 0; s < KSTEPS; s += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 a0 = *reinterpret_cast<const uint4*>(row + 16 * s + 8 * g);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(row + 16 * (s + 1) + 8 * g);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), ws.qreg[s], sc, 0, 0, 0);
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), ws.qreg[s + 1], sc, 0, 0, 0);
+  }
+  if (partial) {
+    const int rel = ws.lim - kbase - 32 * st - 16 * g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r >= rel) sc[r] = -INFINITY;
+  }
+  return sc;
+}
+
+// Rare path, after a step whose tile sum exceeded 2^64 (or overflowed) for
+// some lane: the tile's scores are gone from registers and its K slot is
+// being refilled, so they are recomputed from K in global memory, one 32-key
+// block at a time (twice: for the max, then for P).  The reference moves to
+// the tile max where that is higher, O and the running sum (which already
+// hold P(j-1)) are rescaled, and P(j) and its sum are redone.
+template <int D>
+__device__ __forceinline__ void overflow_tile(const AttnParams& p, WaveState<D>& ws, int head, int kbase, bool partial,
+                              int lane, bf16x8_t (&pcur)[NST][2], float& l_tile) {
+  float mx = -INFINITY;
+#pragma unroll 1
+  for (int st = 0; st < NST; ++st) {
+    const f32x16_t sc = block_scores<D>(p, ws, head, kbase, st, partial, lane);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2)
+      mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[r]), sc[r + 1]);
+  }
+  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  const float m_new = __builtin_elementwise_maximum(ws.m_ref, mx * p.c_log2);
+  const float alpha = m_new > ws.m_ref ? __builtin_amdgcn_exp2f(ws.m_ref - m_new) : 1.f;
+  ws.l_run *= alpha;
+#pragma unroll
+  for (int i = 0; i < WaveState<D>::DT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ws.oacc[i][r] *= alpha;
+  ws.m_ref = m_new;
+  const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+  l_tile = 0.f;
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    const f32x16_t sc = block_scores<D>(p, ws, head, kbase, st, partial, lane);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * t + 2 * e], c, -m_use));
-        const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][8 * t + 2 * e + 1], c, -m_use));
+        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e], p.c_log2, -ws.m_ref));
+        const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * t + 2 * e + 1], p.c_log2, -ws.m_ref));
         w[e] = pack_bf16(a, b);
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones2, l, false);
+        l_tile = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[e]), ones2, l_tile, false);
       }
-      pb[st][t] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+      pcur[st][t] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
     }
-  return l;
-}
-
-// Rare path: move the reference max to this tile's max (per lane), rescale
-// O and the running sum, and redo the exponentials.
-template <int D>
-__device__ inline void rescale_and_exps(WaveState<D>& ws, const f32x16_t (&s)[NST], float c,
-                                        bf16x8_t (&pb)[NST][2], float& l_tile) {
-  float mx = s[0][0];
-#pragma unroll
-  for (int st = 0; st < NST; ++st)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[st][r]);
-  auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-  mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
-  const float m_new = fmaxf(ws.m_ref, mx);
-  if (m_new > ws.m_ref) {  // only rows whose reference moves
-    const float alpha = __builtin_amdgcn_exp2f(ws.m_ref - m_new);
-    ws.l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < WaveState<D>::DT; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ws.oacc[i][r] *= alpha;
-    ws.m_ref = m_new;
+    __builtin_amdgcn_sched_barrier(0);
   }
-  l_tile = exps(s, c, ws.m_ref == -INFINITY ? 0.f : ws.m_ref, pb);
 }
 
-// O^T += V^T P^T for one tile.
-template <int D>
-__device__ inline void pv(WaveState<D>& ws, const unsigned char* vtile, const bf16x8_t (&pb)[NST][2]) {
-  using L = Lay<D>;
-#pragma unroll
-  for (int dt = 0; dt < WaveState<D>::DT; ++dt)
-#pragma unroll
-    for (int st = 0; st < NST; ++st)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const unsigned char* base = vtile + ws.vaddr[dt] + (32 * st + 8 * t) * L::ROWB;
-        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base));
-        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + 4 * L::ROWB));
-        s16x8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        ws.oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8), pb[st][t],
-                                                              ws.oacc[dt], 0, 0, 0);
-      }
-}
-
-template <int D, int W, bool ROPE_Q, bool ROPE_K>
+template <int D, int W, bool ROPE_Q>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma(AttnParams p) {
   using L = Lay<D>;
@@ -302,10 +435,10 @@ void attn_fwd_mfma(AttnParams p) {
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* kring = smem;                  // K tiles j+1, j+2 (ring of 2)
-  unsigned char* vring = smem + 2 * L::TILE_B;  // V tiles j, j+1 (ring of 2)
+  unsigned char* kring = smem;                  // K tiles (ring of 2)
+  unsigned char* vring = smem + 2 * L::TILE_B;  // V tiles (ring of 2)
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const int l32 = lane & 31;
@@ -335,7 +468,7 @@ void attn_fwd_mfma(AttnParams p) {
   const int ntw = wave_live ? (int)((lim_hi + BN - 1) / BN) : 0;
 
   WaveState<D> ws;
-  ws.lim = key_end(p.m, i_abs, i_abs);
+  ws.lim = (int)key_end(p.m, i_abs, i_abs);
   TileLoader<D, W> ld;
   ld.init(wave, lane, p.k_ts, p.v_ts);
 
@@ -347,29 +480,8 @@ void attn_fwd_mfma(AttnParams p) {
     for (int s = 0; s < KSTEPS; ++s)
       raw[s] = row_ok ? *reinterpret_cast<const uint4*>(src + 16 * s + 8 * g) : make_uint4(0, 0, 0, 0);
     if (ROPE_Q && row_ok) {
-      const float* pp = p.q_pos + 3 * my_row;
-      // dims 16s+8g+e (s < KSTEPS/2) pair with the same slot of s + KSTEPS/2
 #pragma unroll
-      for (int s = 0; s < KSTEPS / 2; ++s) {
-        uint32_t lw[4] = {raw[s].x, raw[s].y, raw[s].z, raw[s].w};
-        uint32_t hw[4] = {raw[s + KSTEPS / 2].x, raw[s + KSTEPS / 2].y, raw[s + KSTEPS / 2].z,
-                          raw[s + KSTEPS / 2].w};
-        float y1[8], y2[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          int kk = 16 * s + 8 * g + e;
-          float cs, sn;
-          rope_cs(pp[rope_axis(p.rope, kk)], p.rope.inv_freq[kk], cs, sn);
-          float x1 = __uint_as_float((e & 1) ? (lw[e >> 1] & 0xFFFF0000u) : (lw[e >> 1] << 16));
-          float x2 = __uint_as_float((e & 1) ? (hw[e >> 1] & 0xFFFF0000u) : (hw[e >> 1] << 16));
-          y1[e] = __builtin_fmaf(x1, cs, -x2 * sn);
-          y2[e] = __builtin_fmaf(x1, sn, x2 * cs);
-        }
-        raw[s] = make_uint4(pack_bf16(y1[0], y1[1]), pack_bf16(y1[2], y1[3]),
-                            pack_bf16(y1[4], y1[5]), pack_bf16(y1[6], y1[7]));
-        raw[s + KSTEPS / 2] = make_uint4(pack_bf16(y2[0], y2[1]), pack_bf16(y2[2], y2[3]),
-                                         pack_bf16(y2[4], y2[5]), pack_bf16(y2[6], y2[7]));
-      }
+      for (int s = 0; s < KSTEPS / 2; ++s) rope_chunk_pair<D>(p.rope, p.q_pos + 3 * my_row, s, g, raw[s], raw[s + KSTEPS / 2]);
     }
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) ws.qreg[s] = as_bf16x8(raw[s]);
@@ -400,80 +512,68 @@ void attn_fwd_mfma(AttnParams p) {
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) ws.oacc[i][r] = 0.f;
-  ws.m_ref = -INFINITY;
+  ws.m_ref = 0.f;
   ws.l_run = 0.f;
 
-  // ---- prologue: K(0), V(0), K(1) resident; S(0) computed ----
+  // ---- prologue: K(0), K(1) resident, V slot 1 zeroed; S(0) computed ----
   ld.template issue<true>(p, head, 0, kring);
-  ld.template issue<false>(p, head, 0, vring);
+  for (int i = threadIdx.x; i < L::TILE_B / 16; i += 64 * W)
+    reinterpret_cast<uint4*>(vring + L::TILE_B)[i] = make_uint4(0, 0, 0, 0);
   if (ntiles > 1) ld.template issue<true>(p, head, BN, kring + L::TILE_B);
   wait_vmem0();
   __syncthreads();
-  if (ROPE_K) {
-    rope_k_tile<D, W>(p, 0, kring);
-    if (ntiles > 1) rope_k_tile<D, W>(p, BN, kring + L::TILE_B);
-    __syncthreads();
-  }
   f32x16_t sa[NST], sb[NST];
-  if (ntw > 0) scores<D>(ws, kring, sa);
+  bf16x8_t pa[NST][2], pb[NST][2];
+#pragma unroll
+  for (int st = 0; st < NST; ++st)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) pa[st][t] = as_bf16x8(make_uint4(0, 0, 0, 0));
+  if (ntw > 0) {
+    float unused = 0.f;
+    tile_step<D, true, false, false>(ws, kring, vring, sb, sa, pb, pa, p.c_log2, unused);
+  }
   __syncthreads();  // every wave has read K(0) before step 0 overwrites its slot
 
-  // One pipelined step: tile j's softmax and PV with tile j+1's scores in
-  // flight.  On entry V(j) (V slot j%2) and K(j+1) (K slot (j+1)%2) are
-  // resident; the step starts the copies of K(j+2) into K(j)'s old slot
-  // and of V(j+1) into V(j-1)'s old slot, and waits for both at its end.
-  auto step = [&](int j, f32x16_t (&cur)[NST], f32x16_t (&nxt)[NST]) {
+  // Step j: exponentials of tile j, scores of tile j+1, PV of tile j-1.  On
+  // entry K(j+1) (K slot (j+1)%2) and V(j-1) (V slot (j+1)%2) are resident;
+  // the step starts the copies of K(j+2) into K(j)'s old slot and of V(j)
+  // into V(j-2)'s old slot, and waits for both at its end.  Step ntiles only
+  // finishes the last PV.
+  auto step = [&](int j, f32x16_t (&cur)[NST], f32x16_t (&nxt)[NST], bf16x8_t (&pprev)[NST][2],
+                  bf16x8_t (&pcur)[NST][2]) {
     if (j + 2 < ntiles) ld.template issue<true>(p, head, (int64_t)(j + 2) * BN, kring + (j & 1) * L::TILE_B);
-    if (j + 1 < ntiles)
-      ld.template issue<false>(p, head, (int64_t)(j + 1) * BN, vring + ((j + 1) & 1) * L::TILE_B);
-    if (j < ntw) {
-      const int64_t kbase = (int64_t)j * BN;
-      if (kbase + BN > lim_lo) {  // partial tile: key j is allowed iff j < lim
-        const int64_t rel = ws.lim - kbase;
-        const int lrel = rel < 0 ? 0 : (rel > BN ? BN : (int)rel);
-#pragma unroll
-        for (int st = 0; st < NST; ++st)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * st + 16 * g + r >= lrel) cur[st][r] = -INFINITY;
-      }
-      // One basic block: the MFMAs of S(j+1) interleaved with the
-      // exponentials of tile j.  On a wave's last tile the K slot read here
-      // holds a stale (valid) tile whose scores are never used.
-      bf16x8_t pb[NST][2];
-      const float m_use = ws.m_ref == -INFINITY ? 0.f : ws.m_ref;
-      scores<D>(ws, kring + ((j + 1) & 1) * L::TILE_B, nxt);
-      float l_tile = exps(cur, p.c_log2, m_use, pb);
-      // 4 K reads ahead, then per MFMA: 1 MFMA, 1 K read, 6 VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < NST * WaveState<D>::KSTEPS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-      if (__builtin_amdgcn_ballot_w64(ws.m_ref == -INFINITY || !(l_tile <= RESCALE_SUM)) != 0)
-        rescale_and_exps<D>(ws, cur, p.c_log2, pb, l_tile);
-      ws.l_run += l_tile;
-      pv<D>(ws, vring + (j & 1) * L::TILE_B, pb);
-      // 8 V^T reads ahead, then per MFMA: 1 MFMA, 2 reads
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
-#pragma unroll
-      for (int i = 0; i < NST * 2 * WaveState<D>::DT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    if (j < ntiles) ld.template issue<false>(p, head, (int64_t)j * BN, vring + (j & 1) * L::TILE_B);
+    const unsigned char* kt = kring + ((j + 1) & 1) * L::TILE_B;
+    const unsigned char* vt = vring + ((j + 1) & 1) * L::TILE_B;
+    const bool do_e = j < ntw;
+    const bool do_pv = j >= 1 && j <= ntw;
+    float l_tile = 0.f;
+    const int64_t kbase = (int64_t)j * BN;
+    const bool partial = kbase + BN > lim_lo;  // some key of the tile is masked for some row
+    if (do_e) {
+      if (partial) mask_tile(cur, ws.lim, (int)kbase, g);
+      // The row's reference is its exact max over tile 0 (which holds key 0
+      // for every row); later tiles move it only on overflow.
+      if (__builtin_expect(j == 0, 0)) {
+        const float mq = query_max(cur) * p.c_log2;
+        ws.m_ref = mq > -INFINITY && mq < INFINITY ? mq : 0.f;
       }
     }
-    wait_vmem0();
-    __syncthreads();
-    if (ROPE_K && j + 2 < ntiles) {
-      rope_k_tile<D, W>(p, (int64_t)(j + 2) * BN, kring + (j & 1) * L::TILE_B);
+    // One schedule for every step j <= ntw.  Step 0 multiplies P(-1) = 0
+    // into the zero-filled V slot 1; step ntw computes scores and P for a
+    // tile past the wave's keys from a stale K slot, and never uses them.
+    if (j <= ntw) tile_step<D, true, true, true>(ws, kt, vt, cur, nxt, pprev, pcur, p.c_log2, l_tile);
+    if (__builtin_expect(do_e && __builtin_amdgcn_ballot_w64(!(l_tile <= OVERFLOW_SUM)) != 0, 0))
+      overflow_tile<D>(p, ws, head, (int)kbase, partial, lane, pcur, l_tile);
+    if (do_e) ws.l_run += l_tile;
+    if (j < ntiles) {
+      wait_vmem0();
       __syncthreads();
     }
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, sa, sb);
-    if (j + 1 < ntiles) step(j + 1, sb, sa);
+  for (int j = 0; j <= ntiles; j += 2) {
+    step(j, sa, sb, pa, pb);
+    if (j + 1 <= ntiles) step(j + 1, sb, sa, pb, pa);
   }
 
   // ---- epilogue: merge the two lane halves' sums, normalise, store ----
@@ -499,19 +599,19 @@ void attn_fwd_mfma(AttnParams p) {
   }
 }
 
-template <int D, bool RQ, bool RK>
+template <int D, bool RQ>
 static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   constexpr int W = ATTN_WAVES;
   constexpr int BYTES = Lay<D>::BYTES;
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_mfma<D, W, RQ, RK>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_mfma<D, W, RQ>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, BYTES);
     if (e != hipSuccess) return e;
     configured = true;
   }
   dim3 grid((unsigned)(p.n_qtiles * p.n_heads));
-  hipLaunchKernelGGL((attn_fwd_mfma<D, W, RQ, RK>), grid, dim3(64 * W), BYTES, s, p);
+  hipLaunchKernelGGL((attn_fwd_mfma<D, W, RQ>), grid, dim3(64 * W), BYTES, s, p);
   return hipGetLastError();
 }
 
@@ -531,19 +631,11 @@ hipError_t attention_bf16_mfma(const mot_attn_args* a, const RopeTable& rt, hipS
   float scale = a->scale != 0.f ? a->scale : 1.f / sqrtf((float)a->head_dim);
   p.c_log2 = scale * 1.4426950408889634f;
   p.q_pos = a->q_pos;
-  p.k_pos = a->k_pos;
   p.rope = rt;
-  const bool rq = a->q_pos != nullptr, rk = a->k_pos != nullptr;
-  if (a->head_dim == 128) {
-    if (rq && rk) return launch_attn<128, true, true>(p, s);
-    if (rq) return launch_attn<128, true, false>(p, s);
-    if (rk) return launch_attn<128, false, true>(p, s);
-    return launch_attn<128, false, false>(p, s);
-  }
-  if (rq && rk) return launch_attn<64, true, true>(p, s);
-  if (rq) return launch_attn<64, true, false>(p, s);
-  if (rk) return launch_attn<64, false, true>(p, s);
-  return launch_attn<64, false, false>(p, s);
+  // K is used as given (the caller checks that no k_pos was passed)
+  const bool rq = a->q_pos != nullptr;
+  if (a->head_dim == 128) return rq ? launch_attn<128, true>(p, s) : launch_attn<128, false>(p, s);
+  return rq ? launch_attn<64, true>(p, s) : launch_attn<64, false>(p, s);
 }
 
 }  // namespace mot

@@ -92,6 +92,10 @@ def test_attention_fp32_tiny_workload_full():
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
 @pytest.mark.parametrize("rope_k", [False, True])
 def test_attention_fused_rope_on_load(dtype, d, rope_k):
+    if rope_k and dtype == "bf16":
+        pytest.skip("bf16 rotates Q on load only: a GPU memory fault in the bf16 kernel variant that "
+                    "also rotated K on load had no cause found, so that variant was removed and the "
+                    "library rejects k_pos for bf16 (checked on the host)")
     dev = device()
     mot = _mot()
     wl = W.BY_NAME["policy_bf16"]
@@ -115,6 +119,43 @@ def test_attention_fused_rope_on_load(dtype, d, rope_k):
     kr = omrope.apply(k.f32, pos, secs, 1e4)
     want, _ = oattn.attention(qr, kr, v.f32, 0, AR, n_ar=n_ar)
     assert_parity(to_np(O), want, "bf16" if dtype == "bf16" else "fp32", "fused rope")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("kind", ["jump", "first_tile_low"])
+def test_attention_large_scores_move_the_reference(kind, d):
+    """Scores far above the reference taken on a row's first tile (by 2^77
+    and, for one key, past the fp32 range of exp2) and first tiles far below
+    the rest: the kernel must move its softmax reference on the fly and
+    still match the fp64 oracle."""
+    dev = device()
+    mot = _mot()
+    nq = nk = 600
+    n_ar, h = 100, 2
+    say("attention large scores %s d=%d" % (kind, d))
+    q, k, v = _qkv(11, nq, nk, h, d, "bf16")
+    qf, kf = q.f32.copy(), k.f32.copy()
+    if kind == "jump":
+        qf[n_ar:, :, 0] += 8.0
+        kf[300, :, 0] = 80.0    # ~2^81 above a random first tile's max
+        kf[500, :, 0] = 150.0   # ~2^153: exp2 overflows without a new reference
+    else:
+        qf[n_ar:, :, 0] -= 8.0
+        kf[:64, :, 0] = 80.0    # first tile ~2^-81 below the later ones
+    qb = W.Tensor("bf16", W.bf16_bits(qf), W.bf16_to_f32(W.bf16_bits(qf)))
+    kb = W.Tensor("bf16", W.bf16_bits(kf), W.bf16_to_f32(W.bf16_bits(kf)))
+    Q, K, V = _to_dev(qb, kb, v, dev, packed=True)
+    O = torch.empty((nq, h, d), dtype=torch.bfloat16, device=dev)
+    L = torch.empty((h, nq), dtype=torch.float32, device=dev)
+    mot.mot_attention_fwd(Q, K, V, O, mask=AR, n_ar=n_ar, lse=L)
+    torch.cuda.synchronize()
+    want, lse = oattn.attention(qb.f32, kb.f32, v.f32, 0, AR, n_ar=n_ar)
+    assert_parity(to_np(O), want, "bf16", "large scores " + kind)
+    # The row sum adds the bf16-rounded P that the PV product uses; here many
+    # keys sit just below a row's max, their roundings share a sign, and the
+    # sum's relative error reaches ln(1 + 2^-9) = 1.95e-3 in the LSE, plus the
+    # fp32 error of scores near 1e3 (~1e-4).
+    np.testing.assert_allclose(to_np(L), lse, atol=2.5e-3, rtol=1e-5)
 
 
 def test_attention_ar_rows_bitwise_invariant_to_dm():

@@ -130,6 +130,18 @@ def test_attention_rejects_bad_args(kw):
     assert st == mot.MOT_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("kw", [
+    # bf16 rotates Q on load only; K is rotated beforehand
+    dict(k_pos=4096, sec_t=16, sec_h=24, sec_w=24, theta=1e4),
+    # a 64-row K tile past 4 GiB, and key counts past 32 bits
+    dict(k_ts=1 << 25, k_hs=128),
+    dict(nk=1 << 31),
+])
+def test_attention_bf16_unsupported(kw):
+    st = mot.raw_call("mot_attention_fwd", ctypes.byref(_args(**kw)), None)
+    assert st == mot.MOT_ERR_UNSUPPORTED
+
+
 def test_projection_and_rope_and_euler_reject_bad_args():
     vp = ctypes.c_void_p
     # projection: n_ar > n_rows; unaligned; bf16 with d_in not a multiple of 64
