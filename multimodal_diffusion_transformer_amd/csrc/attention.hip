@@ -10,15 +10,20 @@
 //    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane owns
 //    one column, so every lane owns ONE query and 16 of its keys per
 //    32-key block; row statistics are per-lane scalars and the only
-//    cross-lane step (a permlane32 swap) runs when a reference max moves.
+//    cross-lane step (a permlane32 swap) runs on a row's first tile and when
+//    a reference max moves.
 //  * K rows are fed to the MFMA in a permuted order so that lane half g
 //    ends up holding keys 16g..16g+15 of each 32-key block in register
 //    order.  Those registers, packed to bf16, are exactly the B operand of
 //    O^T += V^T P^T for 8 consecutive keys: P never leaves registers.
-//  * Software pipeline inside each wave: while the softmax of tile j runs on
-//    the vector ALUs, the MFMAs of S for tile j+1 are already in flight;
-//    then P(j) V(j) follows.  K therefore runs one tile ahead of V: K and V
-//    have separate two-stage LDS rings, filled straight from HBM with
+//  * Software pipeline inside each wave, one fixed schedule per key tile:
+//    step j computes the scores of tile j+1 and the PV product of tile j-1
+//    on the MFMA while the vector ALUs run the exponentials of tile j.  The
+//    three streams are independent inside a step, so score and PV MFMAs
+//    alternate, the exponentials are spread evenly between them, each MFMA's
+//    LDS operand is read two MFMAs ahead, and a scheduling fence after every
+//    MFMA keeps that order.  K runs two tiles ahead of V: K and V have
+//    separate two-slot LDS rings, filled straight from HBM with
 //    global_load_lds_dwordx4 (no staging registers, no VALU; issued from
 //    inline asm with vmcnt managed here, so a copy overlaps the compute
 //    before it instead of being drained at the next LDS read).
@@ -29,12 +34,15 @@
 //    both reads bank-conflict free; all LDS addresses are loop-invariant per
 //    lane and tile bases are scalar.
 //  * Q (rotated by mRoPE on load when positions are given) lives in
-//    registers for the whole key loop.
+//    registers for the whole key loop.  K is used as given (rotated
+//    beforehand when positions apply).
 //  * Softmax in fp32 in the log2 domain (scale*log2(e) folded into one FMA
-//    before exp2), against a reference maximum that only moves when a lane's
-//    tile sum exceeds 2^16 (or on a row's first tile): the common tile needs
-//    no max, no cross-lane step and no rescale.  Row sums accumulate the
-//    bf16-packed P with dot2, so numerator and denominator use the same P.
+//    before exp2).  A row's reference is its exact max over its first tile
+//    (which always holds key 0); it moves only if a later tile's sum of P
+//    passes 2^64, in a rare path that recomputes that tile's scores from K
+//    in global memory.  The common tile needs no max, no cross-lane step and
+//    no rescale.  Row sums accumulate the bf16-packed P with dot2, so
+//    numerator and denominator use the same P.
 //  * Both masks give every query a prefix of the keys, [0, key_end(i)).  A
 //    per-lane limit decides each pair with one compare, and the limits of a
 //    wave's first and last rows classify its tiles exactly: tiles past a
