@@ -119,9 +119,16 @@ def main():
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--rocprof-summary", metavar="DIR",
                     help="only summarise rocprofv3 CSV output under DIR (no GPU use)")
+    ap.add_argument("--write-profiles", metavar="DIR",
+                    help="only write the profiles/ summaries from the rocprofv3 runs under DIR "
+                         "(prof_bench, pmc_fetch, pmc_write, pmc_copy_fetch, pmc_copy_write, "
+                         "pmc_sq; see the commands in the files written), no GPU use")
     args = ap.parse_args()
     if args.rocprof_summary:
         print(rocprof_summary(args.rocprof_summary))
+        return
+    if args.write_profiles:
+        write_profiles(args.write_profiles, args.workload)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the multi-GPU path (head-sharded attention "
@@ -255,6 +262,97 @@ def rocprof_summary(d):
             out.append("  %-48s %-14s dispatches %4d  mean %.6g" % (name, cname, len(vals),
                                                                   sum(vals) / len(vals)))
     return "\n".join(out)
+
+
+def _counter_mean(d, kernel, counter):
+    """Mean over dispatches of `kernel` of one counter (summed over its
+    instances within a dispatch), from rocprofv3 CSV output under d."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    per = defaultdict(float)
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if kernel in row["Kernel_Name"] and row["Counter_Name"] == counter:
+                    per[row["Dispatch_Id"]] += float(row["Counter_Value"])
+    if not per:
+        raise SystemExit("no %s samples of %s under %s" % (counter, kernel, d))
+    return sum(per.values()) / len(per), len(per)
+
+
+def write_profiles(d, workload):
+    """Write profiles/<kernel>_<workload>_{kernel_stats,hbm_traffic,sq_counters}.txt
+    from the rocprofv3 CSV runs under d (the commands are recorded in each)."""
+    pre = os.path.join(ROOT, "profiles", "%s_%s" % (ATTN_KERNEL, workload))
+    cmd_head = ("commands (run on an MI355X from the repository root; <repo> is its absolute path,\n"
+                "<out> the output folder):\n  cd /tmp && export TMPDIR=/tmp\n")
+    bench = "python3 <repo>/bench.py --workload %s" % workload
+    h = attention_source_hash()
+    flops = "7.815 TFLOP per launch (635,963,395 allowed pairs x 24 heads x 512 flop)" \
+        if workload == "t2v480p_bf16" else "see DESIGN"
+    # 1. kernel durations
+    txt = ("Kernel durations of one benchmark run of %s; one step = QKV projection, mRoPE of K,\n"
+           "attention (Q rotated on load), O projection, Euler update.\n\n" % workload + cmd_head +
+           "  rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_bench -o bench -- "
+           "%s --steps 5 --warmup 2 --no-cpu-baseline\n" % bench +
+           "  python3 bench.py --write-profiles <out>\n\n"
+           "attention_source_hash: %s\nattention: %s\n\n" % (h, flops) +
+           rocprof_summary(os.path.join(d, "prof_bench")) + "\n")
+    with open(pre + "_kernel_stats.txt", "w") as f:
+        f.write(txt)
+    # 2. HBM traffic, scaled by a copy of known size
+    kib = 1024 * 1024
+    cf, _ = _counter_mean(os.path.join(d, "pmc_copy_fetch"), "copyBuffer", "FETCH_SIZE")
+    cw, _ = _counter_mean(os.path.join(d, "pmc_copy_write"), "copyBuffer", "WRITE_SIZE")
+    ff, fw = kib / cf, kib / cw
+    af, na = _counter_mean(os.path.join(d, "pmc_fetch"), ATTN_KERNEL, "FETCH_SIZE")
+    aw, _ = _counter_mean(os.path.join(d, "pmc_write"), ATTN_KERNEL, "WRITE_SIZE")
+    fb, wb = af * ff * 1024, aw * fw * 1024
+    txt = ("%s on %s: HBM traffic per launch from rocprofv3 counters, each scaled by what the same\n"
+           "counter reads for a device copy of known size.\n\n" % (ATTN_KERNEL, workload) + cmd_head +
+           "".join("  rocprofv3 --pmc %s --output-format csv -d <out>/%s -o %s -- %s\n" % (c, o, n, a)
+                   for c, o, n, a in [
+                       ("FETCH_SIZE", "pmc_fetch", "bench", bench + " --steps 2 --warmup 1 --no-cpu-baseline"),
+                       ("WRITE_SIZE", "pmc_write", "bench", bench + " --steps 2 --warmup 1 --no-cpu-baseline"),
+                       ("FETCH_SIZE", "pmc_copy_fetch", "copy", bench + " --copy-calibration 1024"),
+                       ("WRITE_SIZE", "pmc_copy_write", "copy", bench + " --copy-calibration 1024")]) +
+           "  python3 bench.py --write-profiles <out>\n\n"
+           "calibration: a 1 GiB device copy (__amd_rocclr_copyBuffer, 1,048,576 KiB read and written)\n"
+           "  FETCH_SIZE reads %.1f KiB per dispatch -> fetch factor %.5f\n"
+           "  WRITE_SIZE reads %.1f KiB per dispatch -> write factor %.5f\n\n" % (cf, ff, cw, fw) +
+           "attention, mean per dispatch (%d dispatches each):\n" % na +
+           "  FETCH_SIZE %.1f KiB x %.5f = %.4f GB\n  WRITE_SIZE %.1f KiB x %.5f = %.4f GB\n"
+           % (af, ff, fb / 1e9, aw, fw, wb / 1e9) +
+           "  algorithmic bytes: Q + K + V read once, O written once = 4 x N x H x D x 2 B\n\n"
+           "attention_source_hash: %s\nfetch_bytes_per_launch: %.0f\nwrite_bytes_per_launch: %.0f\n"
+           "traffic_bytes_per_launch: %.0f\n\nraw summaries:\n" % (h, fb, wb, fb + wb) +
+           "\n".join(rocprof_summary(os.path.join(d, x))
+                     for x in ("pmc_fetch", "pmc_write", "pmc_copy_fetch", "pmc_copy_write")) + "\n")
+    with open(pre + "_hbm_traffic.txt", "w") as f:
+        f.write(txt)
+    # 3. shader counters of the attention kernel
+    sq = os.path.join(d, "pmc_sq")
+    if os.path.isdir(sq):
+        names = ["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU",
+                 "SQ_LDS_BANK_CONFLICT"]
+        vals = {n: _counter_mean(sq, ATTN_KERNEL, n)[0] for n in names}
+        txt = ("%s on %s: shader counters, mean per dispatch.\n\n" % (ATTN_KERNEL, workload) + cmd_head +
+               "  rocprofv3 --pmc %s --output-format csv -d <out>/pmc_sq -o bench -- %s --steps 2 --warmup 1"
+               " --no-cpu-baseline\n  python3 bench.py --write-profiles <out>\n\n" % (" ".join(names), bench) +
+               "attention_source_hash: %s\n\n" % h +
+               "".join("  %-26s %.6g\n" % (n, vals[n]) for n in names) +
+               "\nderived:\n"
+               "  MFMA busy cycles per MFMA instruction: %.2f (a 32x32x16 bf16 MFMA occupies the unit 32 cycles)\n"
+               "  non-MFMA VALU instructions per MFMA: %.2f\n"
+               "  LDS instructions per MFMA: %.2f\n" % (
+                   vals["SQ_VALU_MFMA_BUSY_CYCLES"] / vals["SQ_INSTS_MFMA"],
+                   (vals["SQ_INSTS_VALU"] - vals["SQ_INSTS_MFMA"]) / vals["SQ_INSTS_MFMA"],
+                   vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"]))
+        with open(pre + "_sq_counters.txt", "w") as f:
+            f.write(txt)
 
 
 if __name__ == "__main__":
