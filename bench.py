@@ -152,6 +152,8 @@ def main():
     from multimodal_diffusion_transformer_amd import pipeline
 
     wl = W.BY_NAME[args.workload]
+    if wl.mask == W.CHUNK_CAUSAL_KV:
+        return bench_stream(args, wl)
     dev = torch.device("cuda:0")
     n, hid, h, d = wl.n_tokens, wl.hidden, wl.n_heads, wl.head_dim
     n_ar, n_clean, n_noisy = W.region_counts(wl.segments)
@@ -262,6 +264,102 @@ def rocprof_summary(d):
             out.append("  %-48s %-14s dispatches %4d  mean %.6g" % (name, cname, len(vals),
                                                                   sum(vals) / len(vals)))
     return "\n".join(out)
+
+
+def bench_stream(args, wl):
+    """Streaming rollout: per chunk, `stream_steps` denoising steps of
+    chunk-causal attention against the rolling cache (the chunk's keys are
+    rotated into the cache tail, Q is rotated on load), then the chunk moves
+    into its ring slot.  One timed step = one whole rollout of
+    `stream_chunks` chunks; inputs are synthetic and already on the device."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from multimodal_diffusion_transformer_amd import pipeline
+
+    dev = torch.device("cuda:0")
+    h, d = wl.n_heads, wl.head_dim
+    ft = wl.stream_views * wl.stream_gh * wl.stream_gw
+    slots = wl.stream_history_frames
+    n_prefix = wl.stream_text + 2
+    pos, _, n_ar = W_layout(wl)
+    nhist = n_prefix + slots * ft
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.wid)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    st = pipeline.StreamState(h, d, n_prefix, ft, slots, wl.sections, wl.theta, device=dev)
+    st.fill(randn(nhist, h, d), randn(nhist, h, d), torch.from_numpy(pos[:nhist]).to(dev))
+    n_calls = wl.stream_chunks * wl.stream_steps
+    qs = [randn(ft, h, d) for _ in range(n_calls)]
+    ks = [randn(ft, h, d) for _ in range(n_calls)]
+    vs = [randn(ft, h, d) for _ in range(n_calls)]
+    t0 = n_ar + 15000.0
+    cps = []
+    for c in range(wl.stream_chunks):
+        cp = pos[nhist:nhist + ft].copy()
+        cp[:, 0] = np.float32(t0 + slots + c)
+        cps.append(torch.from_numpy(cp).to(dev))
+    O = torch.empty((ft, h, d), dtype=torch.bfloat16, device=dev)
+
+    def rollout(ev=None):
+        i = 0
+        for c in range(wl.stream_chunks):
+            for s in range(wl.stream_steps):
+                if ev is not None:
+                    ev[i][0].record()
+                st.attend(qs[i], ks[i], vs[i], cps[c], O)
+                if ev is not None:
+                    ev[i][1].record()
+                i += 1
+            st.append(c)
+
+    for _ in range(args.warmup):
+        rollout()
+    torch.cuda.synchronize()
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(n_calls)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(args.steps):
+        rollout(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    per_call = [evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps) for i in range(n_calls)]
+    pairs = ft * (nhist + ft)  # the chunk is the newest: every row sees the whole cache
+    call_flops = 4.0 * d * h * pairs
+    ms_step = wall * 1e3 / args.steps
+    value = call_flops * n_calls / (ms_step * 1e-3) / 1e12
+    med = float(np.median(per_call))
+    line = {
+        "metric": "MoT masked-attention TFLOP/s (unmasked pairs) + % of MI355X bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) queries, keys and values)",
+        "config": {"workload": "%s: chunk-causal streaming, %d-token chunks (one latent frame, %d views "
+                               "x %dx%d) against a %d-key cache (%d prefix + %d history frames), "
+                               "%d chunks x %d steps per rollout"
+                               % (wl.name, ft, wl.stream_views, wl.stream_gh, wl.stream_gw, nhist + ft,
+                                  n_prefix, slots, wl.stream_chunks, wl.stream_steps),
+                   "heads": h, "head_dim": d, "mask": "CHUNK_CAUSAL_KV",
+                   "step": "per call: K/V chunk into the cache + mRoPE(K chunk) + attention (Q on load)"},
+        "attention_call_ms": {"median": round(med, 4), "min": round(float(np.min(per_call)), 4)},
+        "attention_call_tflops_median": round(call_flops / (med * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL,
+                     "achieved": round(call_flops / (med * 1e-3) / 1e12, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(call_flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def W_layout(wl):
+    from multimodal_diffusion_transformer_amd import _binding as B
+    return B.mot_build_layout(wl.segments)
 
 
 def _counter_mean(d, kernel, counter):
