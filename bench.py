@@ -34,11 +34,18 @@ ATTN_SOURCES = ("multimodal_diffusion_transformer_amd/csrc/attention.hip",
 
 
 def attention_source_hash():
+    """Hash of the attention sources with comments and blank space removed,
+    so that it changes when the code does and not when its comments do."""
     import hashlib
+    import re
+
     h = hashlib.sha256()
     for rel in ATTN_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

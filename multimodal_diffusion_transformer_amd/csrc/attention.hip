@@ -123,6 +123,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // inline asm so the compiler does not drain every outstanding copy before
 // each LDS read (it cannot tell that the copies target another stage); the
 // kernel waits on vmcnt itself.  The instruction has no VGPR result.
+//
+// Hazard: the hardware needs wait states between a VALU write of an SGPR and
+// a vector-memory instruction reading it, and the compiler inserts none in
+// front of inline asm.  The base must therefore reach the SGPR pair through
+// scalar instructions (as every tile base here does: it is built from
+// kernel arguments and wave-uniform loop counters); a base that only exists
+// in VGPRs, moved over by v_readfirstlane right before the copy, makes the
+// copy read a stale base.  A host test scans the built library for that
+// pattern.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   // the tile base is wave-uniform by construction; make it an SGPR pair
   // (readfirstlane returns int: go through uint32_t so nothing sign-extends)

@@ -192,6 +192,214 @@ __global__ __launch_bounds__(256) void gemm_region_bf16(GemmParams p) {
   }
 }
 
+// ---- bf16 path, direct-to-LDS tiles (switched off) ----
+//
+// Built only with -DMOT_GEMM_DMA=1.  Its first GPU test faulted; the cause
+// (a copy reading a base that a VALU wrote with no wait states in between)
+// is fixed below, but the fixed kernel has not run on a GPU yet, so the
+// library keeps the register-staged kernel above.
+#if defined(MOT_GEMM_DMA) && MOT_GEMM_DMA
+//
+// Workgroup tile 256 rows x 128 cols, 32-deep stages, two LDS stages (48 KB),
+// 4 waves each owning 128 rows x 64 cols as 4x2 v_mfma_f32_32x32x16_bf16
+// blocks of Y^T = W^T X^T.  Both operands go from HBM straight into LDS with
+// global_load_lds_dwordx4 (no staging registers, no VALU):
+//  * W tile [32 k][128 n], 256-byte rows, 16-byte chunks XOR-swizzled by
+//    4 (k % 4); read transposed (W^T) with ds_read_b64_tr_b16;
+//  * X tile [256 m][32 k], 64-byte rows, chunks XOR-swizzled by (m / 4) % 2;
+//    read with ds_read_b128.
+// Both reads are bank-conflict free.  The next stage's copies are issued at
+// the start of a stage and waited for at its end; inside a stage the second
+// k-step's operands are read under the first k-step's MFMAs.
+constexpr int HM = 256;   // rows per workgroup
+constexpr int HN = 128;   // cols per workgroup
+constexpr int HK = 32;    // depth per stage
+constexpr int H_WB = HK * HN * 2;             // W tile bytes (8 KB)
+constexpr int H_XB = HM * HK * 2;             // X tile bytes (16 KB)
+constexpr int H_STAGE = H_WB + H_XB;          // 24 KB
+constexpr int H_SMEM_BYTES = 2 * H_STAGE;     // 48 KB
+static_assert(H_SMEM_BYTES <= 65536, "LDS copies stay below 64 KB");
+
+// One wave-wide 16-byte-per-lane copy from global memory (scalar base +
+// per-lane unsigned 32-bit offset) into LDS at `lds` + 16 * lane.  Here the
+// tile bases are computed on the vector ALUs (block -> tile division) and
+// reach the SGPR pair through v_readfirstlane; the hardware needs 5 wait
+// states between that VALU write of an SGPR and the copy that reads it, and
+// the compiler inserts none in front of inline asm, so the asm provides them.
+__device__ __forceinline__ void g_dma16(const void* gbase, uint32_t voff, uint32_t lds) {
+  const uint64_t b = (uint64_t)gbase;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ uint32_t g_lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void g_wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef short g_s16x4_t __attribute__((ext_vector_type(4)));
+typedef short g_s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) g_s16x4_t g_lds_s16x4_t;
+
+// Issue this wave's copies of one stage: W rows [k0, k0+32) x cols [n0, n0+128)
+// (2 loads of 4 rows) and X rows [r0, r0+256) of the problem x k [k0, k0+32)
+// (4 loads of 16 rows).  Columns past N and rows past the problem re-read
+// the last valid ones: never out of range, never stored.
+__device__ __forceinline__ void h_issue(const GemmParams& p, const bf16_t* w, int64_t r0, int64_t rows,
+                                        int64_t n0, int64_t k0, int wave, int lane, uint32_t lw,
+                                        uint32_t lx, unsigned char* dst) {
+  const int64_t N = p.N, K = p.K;
+  const char* wb = reinterpret_cast<const char*>(w) + (k0 * N + n0) * 2;
+  const bool ragged_n = n0 + HN > N;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int i = 2 * wave + t;  // rows 4i .. 4i+3 of the W tile
+    if (__builtin_expect(!ragged_n, 1)) {
+      g_dma16(wb + (int64_t)4 * i * N * 2, lw, g_lds_addr(dst + i * 1024));
+    } else {
+      const int row = 4 * i + lane / 16;
+      int c = (lane % 16) ^ (4 * (row & 3));  // logical chunk of this lane's slot
+      const int last_c = (int)((N - n0) / 8) - 1;
+      if (c > last_c) c = last_c;
+      g_dma16(wb, (uint32_t)((int64_t)row * N * 2 + c * 16), g_lds_addr(dst + i * 1024));
+    }
+  }
+  const char* xb = reinterpret_cast<const char*>(p.x) + (r0 * K + k0) * 2;
+  const bool ragged_m = rows < HM;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int i = 4 * wave + t;  // rows 16i .. 16i+15 of the X tile
+    if (__builtin_expect(!ragged_m, 1)) {
+      g_dma16(xb + (int64_t)16 * i * K * 2, lx, g_lds_addr(dst + H_WB + i * 1024));
+    } else {
+      int64_t row = 16 * i + lane / 4;
+      const int c = (lane % 4) ^ ((int)(row >> 2) & 1);
+      if (row > rows - 1) row = rows - 1;
+      g_dma16(xb, (uint32_t)(row * K * 2 + c * 16), g_lds_addr(dst + H_WB + i * 1024));
+    }
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_region_mfma(GemmParams p) {
+  extern __shared__ __align__(16) unsigned char hsm[];
+  int b = blockIdx.x;
+  int prob = 0;
+  const int per0 = p.tiles_m[0] * p.tiles_n;
+  if (b >= per0) { prob = 1; b -= per0; }
+  const int tn = b % p.tiles_n;
+  const int tm = b / p.tiles_n;
+  const int64_t r0 = p.row0[prob] + (int64_t)tm * HM;
+  int64_t rows = p.rows[prob] - (int64_t)tm * HM;
+  if (rows > HM) rows = HM;
+  const int64_t n0 = (int64_t)tn * HN;
+  const bf16_t* w = p.w[prob];
+
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int wm = wave & 1, wn = wave >> 1;  // wave's rows [128 wm, +128), cols [64 wn, +64)
+
+  // loop-invariant lane offsets of the copies (bytes, from the tile base)
+  const uint32_t lw = (uint32_t)((int64_t)(lane / 16) * p.N * 2 + 16 * ((lane % 16) ^ (4 * ((lane / 16) & 3))));
+  const uint32_t lx = (uint32_t)((int64_t)(lane / 4) * p.K * 2 + 16 * ((lane % 4) ^ ((lane >> 4) & 1)));
+  // LDS operand offsets within a stage, k-step 0: W^T (transposed reads) for
+  // the wave's two 32-col blocks, X for its four 32-row blocks
+  uint32_t aoff[2];
+  {
+    const int j = lane & 15, q16 = (lane >> 4) & 1;
+    const int row = 8 * g + j / 4;  // + 16 s (+ 4 for the upper half): row % 4 unchanged
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int c = 8 * wn + 4 * nb + 2 * q16 + (j & 3) / 2;
+      aoff[nb] = row * (HN * 2) + ((c ^ (4 * (row & 3))) * 16) + 8 * (j & 1);
+    }
+  }
+  const uint32_t boff = (128 * wm + l32) * (HK * 2) + ((g ^ ((l32 >> 2) & 1)) * 16);
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int ksteps = (int)(p.K / HK);
+  h_issue(p, w, r0, rows, n0, 0, wave, lane, lw, lx, hsm);
+  g_wait_vmem0();
+  __syncthreads();
+  for (int kt = 0; kt < ksteps; ++kt) {
+    unsigned char* cur = hsm + (kt & 1) * H_STAGE;
+    if (kt + 1 < ksteps)
+      h_issue(p, w, r0, rows, n0, (int64_t)(kt + 1) * HK, wave, lane, lw, lx, hsm + ((kt + 1) & 1) * H_STAGE);
+    const unsigned char* wt = cur;
+    const unsigned char* xt = cur + H_WB;
+    bf16x8_t a[2][2], bx[2][4];  // [k-step][block]
+    auto read_a = [&](int s, int nb) {
+      const unsigned char* base = wt + aoff[nb] + 16 * s * (HN * 2);
+      g_s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((g_lds_s16x4_t*)(base));
+      g_s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((g_lds_s16x4_t*)(base + 4 * (HN * 2)));
+      g_s16x8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      a[s][nb] = __builtin_bit_cast(bf16x8_t, v);
+    };
+    auto read_b = [&](int s, int mb) {
+      bx[s][mb] = g_as_bf16x8(*reinterpret_cast<const uint4*>(xt + boff + mb * 32 * (HK * 2) + 32 * s));
+    };
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) read_a(0, nb);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) read_b(0, mb);
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 0: 8 MFMAs, each followed by one operand read of k-step 1
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int mb = q / 2, nb = q % 2;
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][nb], bx[0][mb], acc[nb][mb], 0, 0, 0);
+      if (q < 2) read_a(1, q);
+      else if (q < 6) read_b(1, q - 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int mb = q / 2, nb = q % 2;
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][nb], bx[1][mb], acc[nb][mb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    g_wait_vmem0();
+    __syncthreads();
+  }
+  // acc[nb][mb]: Y^T block; the lane owns output row m = 128 wm + 32 mb + l32
+  // and columns n = 64 wn + 32 nb + 8 (r / 4) + 4 g + r % 4
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int mloc = 128 * wm + 32 * mb + l32;
+    if (mloc >= rows) continue;
+    const int64_t row = r0 + mloc;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int64_t n = n0 + 64 * wn + 32 * nb + 8 * rr + 4 * g;
+        if (n >= p.N) continue;
+        if (OUT_BF16) {
+          uint2 v;
+          v.x = g_pack_bf16(acc[nb][mb][4 * rr + 0], acc[nb][mb][4 * rr + 1]);
+          v.y = g_pack_bf16(acc[nb][mb][4 * rr + 2], acc[nb][mb][4 * rr + 3]);
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.y) + row * p.N + n) = v;
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + row * p.N + n) =
+              make_float4(acc[nb][mb][4 * rr + 0], acc[nb][mb][4 * rr + 1], acc[nb][mb][4 * rr + 2],
+                          acc[nb][mb][4 * rr + 3]);
+        }
+      }
+  }
+}
+
+#endif  // MOT_GEMM_DMA
+
 // ---- fp32 VALU path ----
 constexpr int FT = 16;
 
@@ -236,10 +444,32 @@ hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* 
   p.y = y;
   p.row0[0] = 0; p.rows[0] = n_ar;
   p.row0[1] = n_ar; p.rows[1] = n_rows - n_ar;
+  p.K = K; p.N = N;
+#if defined(MOT_GEMM_DMA) && MOT_GEMM_DMA
+  if (K % HK == 0 && N % 64 == 0) {  // direct-to-LDS MFMA kernel
+    const int ob = out_dt == MOT_BF16 ? 1 : 0;
+    p.tiles_m[0] = (int)((p.rows[0] + HM - 1) / HM);
+    p.tiles_m[1] = (int)((p.rows[1] + HM - 1) / HM);
+    p.tiles_n = (int)((N + HN - 1) / HN);
+    const int64_t blocks = (int64_t)(p.tiles_m[0] + p.tiles_m[1]) * p.tiles_n;
+    if (blocks == 0) return hipSuccess;
+    static bool configured_dma[2] = {false, false};
+    const void* fn = ob ? (const void*)gemm_region_mfma<true> : (const void*)gemm_region_mfma<false>;
+    if (!configured_dma[ob]) {
+      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, H_SMEM_BYTES);
+      if (e != hipSuccess) return e;
+      configured_dma[ob] = true;
+    }
+    if (ob)
+      hipLaunchKernelGGL(gemm_region_mfma<true>, dim3((unsigned)blocks), dim3(256), H_SMEM_BYTES, s, p);
+    else
+      hipLaunchKernelGGL(gemm_region_mfma<false>, dim3((unsigned)blocks), dim3(256), H_SMEM_BYTES, s, p);
+    return hipGetLastError();
+  }
+#endif
   p.tiles_m[0] = (int)((p.rows[0] + GM - 1) / GM);
   p.tiles_m[1] = (int)((p.rows[1] + GM - 1) / GM);
   p.tiles_n = (int)((N + GN - 1) / GN);
-  p.K = K; p.N = N;
   const int64_t blocks = (int64_t)(p.tiles_m[0] + p.tiles_m[1]) * p.tiles_n;
   if (blocks == 0) return hipSuccess;
   static bool configured[2] = {false, false};

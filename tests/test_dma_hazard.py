@@ -1,0 +1,75 @@
+"""Host-side check of the built library's gfx950 machine code: no LDS-DMA
+copy (global_load_lds_*) may take its scalar base from an SGPR pair that a
+vector instruction (v_readfirstlane) wrote just before.  The hardware needs
+wait states between a VALU write of an SGPR and a vector-memory read of it,
+and the compiler inserts none in front of the inline asm that issues these
+copies; a stale base makes the copy read from a wrong address."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "multimodal_diffusion_transformer_amd", "libmotattn.so")
+LLVM = "/opt/rocm/llvm/bin"
+WINDOW = 8     # instructions looked back from each copy
+WAIT_STATES = 5  # required between a VALU write of an SGPR and a vector-memory read of it
+
+
+def _kernels(tmp_path):
+    fb = tmp_path / "fatbin"
+    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section", ".hip_fatbin=%s" % fb, LIB],
+                   check=True)
+    data = fb.read_bytes()
+    starts = [m.start() for m in re.finditer(re.escape(b"__CLANG_OFFLOAD_BUNDLE__"), data)]
+    out = {}
+    for n, (a, b) in enumerate(zip(starts, starts[1:] + [len(data)])):
+        bundle = tmp_path / ("b%d" % n)
+        bundle.write_bytes(data[a:b])
+        co = tmp_path / ("b%d.co" % n)
+        r = subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle", "--type=o",
+                            "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", "--input=%s" % bundle,
+                            "--output=%s" % co], capture_output=True)
+        if r.returncode or not co.exists():
+            continue
+        dis = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", "--mcpu=gfx950", str(co)],
+                             capture_output=True, text=True, check=True).stdout.split("\n")
+        name = None
+        for line in dis:
+            m = re.match(r"^[0-9a-f]+ <(.*)>:", line)
+            if m:
+                name = m.group(1)
+                out[name] = []
+            elif name is not None and line.strip():
+                out[name].append(line.strip())
+    return out
+
+
+@pytest.mark.skipif(not os.path.exists(LIB) or not os.path.exists(os.path.join(LLVM, "llvm-objdump")),
+                    reason="library not built or ROCm LLVM tools missing")
+def test_no_lds_dma_reads_a_vector_written_base(tmp_path):
+    kernels = _kernels(tmp_path)
+    assert any("attn_fwd_mfma" in k for k in kernels), "attention kernels not found in the build"
+    copies = bad = 0
+    report = []
+    for name, ins in kernels.items():
+        for i, line in enumerate(ins):
+            m = re.search(r"global_load_lds_dword\w*\s+v\d+,\s+s\[(\d+):(\d+)\]", line)
+            if not m:
+                continue
+            copies += 1
+            regs = {m.group(1), m.group(2)}
+            waits = 0  # wait states between the candidate writer and the copy
+            for prev in reversed(ins[max(0, i - WINDOW):i]):
+                w = re.search(r"v_readfirstlane_b32\s+s(\d+),", prev)
+                if w and w.group(1) in regs:
+                    if waits < WAIT_STATES:
+                        bad += 1
+                        report.append("%s: %s" % (name[:60], line))
+                    break
+                n = re.search(r"s_nop\s+(0x[0-9a-f]+|\d+)", prev)
+                waits += int(n.group(1), 0) + 1 if n else 1
+    assert copies > 0, "no LDS-DMA copies found"
+    assert bad == 0, "copies with a VALU-written base:\n" + "\n".join(report[:10])
