@@ -1,0 +1,71 @@
+"""Host logic of bench.py (no GPU): the algorithmic work it divides by, the
+gating of the recorded HBM traffic on the attention sources, and the
+rocprofv3 CSV summaries it writes into profiles/."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads as W  # noqa: E402
+from oracle import mask as omask  # noqa: E402
+
+
+@pytest.mark.parametrize("name", ["policy_bf16", "t2v480p_bf16", "t2v480p_long_bf16"])
+def test_attention_pairs_equal_the_mask_count(name):
+    wl = W.BY_NAME[name]
+    n, n_ar = wl.n_tokens, W.region_counts(wl.segments)[0]
+    assert bench.attention_pairs(n, n_ar) == omask.count_pairs(n, n, 0, W.AR_CAUSAL_DM_FULL, n_ar=n_ar)
+
+
+def test_480p_flops_per_launch():
+    wl = W.BY_NAME["t2v480p_bf16"]
+    n, n_ar = wl.n_tokens, W.region_counts(wl.segments)[0]
+    pairs = bench.attention_pairs(n, n_ar)
+    assert pairs == 635_963_395
+    assert abs(4.0 * wl.head_dim * wl.n_heads * pairs - 7.815e12) < 1e9
+
+
+def test_traffic_is_read_only_for_the_profiled_sources(monkeypatch):
+    rec = bench.traffic_from_profile("t2v480p_bf16")
+    assert rec is not None and rec > 0.6e9  # at least Q, K, V read and O written once
+    monkeypatch.setattr(bench, "attention_source_hash", lambda: "0" * 16)
+    assert bench.traffic_from_profile("t2v480p_bf16") is None
+    assert bench.traffic_from_profile("no_such_workload") is None
+
+
+def test_source_hash_ignores_comments(tmp_path, monkeypatch):
+    a = tmp_path / "a.hip"
+    a.write_text("int f() { return 1; }  // one\n/* block\ncomment */\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "ATTN_SOURCES", ("a.hip",))
+    h1 = bench.attention_source_hash()
+    a.write_text("int f() {\n  return 1;\n}  // another comment\n")
+    assert bench.attention_source_hash() == h1
+    a.write_text("int f() { return 2; }\n")
+    assert bench.attention_source_hash() != h1
+
+
+def test_rocprof_summaries_parse_csv(tmp_path):
+    (tmp_path / "x_kernel_stats.csv").write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void mot::attn_fwd_mfma<128, 4, true>(mot::AttnParams)",2,200,100.0,75.0,90,110,10\n')
+    (tmp_path / "x_counter_collection.csv").write_text(
+        '"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"\n'
+        '1,"void mot::attn_fwd_mfma<128, 4, true>(mot::AttnParams)","FETCH_SIZE",10\n'
+        '1,"void mot::attn_fwd_mfma<128, 4, true>(mot::AttnParams)","FETCH_SIZE",5\n'
+        '2,"void mot::attn_fwd_mfma<128, 4, true>(mot::AttnParams)","FETCH_SIZE",25\n')
+    text = bench.rocprof_summary(str(tmp_path))
+    assert "attn_fwd_mfma" in text and "100" in text
+    mean, n = bench._counter_mean(str(tmp_path), "attn_fwd_mfma", "FETCH_SIZE")
+    assert n == 2 and mean == 20.0  # per dispatch: 15 and 25
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr

@@ -113,3 +113,38 @@ def test_rows_helper_matches_full():
 
 def test_flop_count_definition():
     assert attention.flops(635963395, 24, 128) == pytest.approx(7.815e12, rel=1e-3)
+
+
+def test_single_key_row_lse_is_its_score():
+    """Row 0 of the AR-causal mask sees key 0 alone: LSE = q0.k0 * scale."""
+    q, k, v = _rand((6, 2, 16), 11), _rand((6, 2, 16), 12), _rand((6, 2, 16), 13)
+    _, lse = attention.attention(q, k, v, 0, AR, n_ar=4)
+    want = (q[0] * k[0]).sum(axis=1) / 4.0  # scale = 1/sqrt(16)
+    np.testing.assert_allclose(lse[:, 0], want, rtol=0, atol=1e-14)
+
+
+def test_two_key_row_is_a_logistic_mix():
+    """Row 1 of the AR-causal mask sees keys 0 and 1: the softmax reduces to a
+    logistic weight w = 1 / (1 + exp(s1 - s0)) and LSE = s0 + log1p(exp(s1 - s0))."""
+    q, k, v = _rand((5, 3, 8), 21), _rand((5, 3, 8), 22), _rand((5, 3, 8), 23)
+    o, lse = attention.attention(q, k, v, 0, AR, n_ar=5)
+    sc = 1.0 / np.sqrt(8.0)
+    for h in range(3):
+        s0 = float(q[1, h] @ k[0, h]) * sc
+        s1 = float(q[1, h] @ k[1, h]) * sc
+        w0 = 1.0 / (1.0 + np.exp(s1 - s0))
+        np.testing.assert_allclose(o[1, h], w0 * v[0, h] + (1.0 - w0) * v[1, h], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[h, 1], s0 + np.log1p(np.exp(s1 - s0)), rtol=0, atol=1e-13)
+
+
+def test_huge_scores_stay_finite():
+    """Scores of +-1e3 (far past exp's range) must go through the max
+    subtraction: O is the value of the dominant key and LSE its score."""
+    d = 4
+    q = np.zeros((3, 1, d)); q[:, 0, 0] = 1.0
+    k = np.zeros((3, 1, d)); k[:, 0, 0] = [0.0, 2000.0, -2000.0]
+    v = _rand((3, 1, d), 31)
+    o, lse = attention.attention(q, k, v, 0, AR, n_ar=0)  # all DM: every row sees all keys
+    for i in range(3):
+        np.testing.assert_allclose(o[i, 0], v[1, 0], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(lse[0, i], 1000.0, rtol=0, atol=1e-12)  # 2000 * 1/sqrt(4)
