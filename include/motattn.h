@@ -19,8 +19,10 @@
  *     nothing was enqueued.  MOT_ERR_HIP reports a failed launch.  Outputs
  *     are undefined after any status other than MOT_OK.
  *   - Device pointers are caller-owned device memory (e.g. torch tensors).
- *     The library allocates no device memory and keeps no mutable global
- *     state; calls are thread-safe.
+ *     The library allocates no device memory.  Its only global state is a
+ *     per-kernel flag recording that the kernel's LDS size attribute was set
+ *     (set once, idempotent); calls are thread-safe.  One device per
+ *     process is assumed: the flag is not per device.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device calls only enqueue work on it; they never synchronize.
  *   - bf16 is bfloat16 (1-8-7), stored as 16-bit words; fp32 is IEEE float.
