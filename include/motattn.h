@@ -8,7 +8,9 @@
  *       §2 packed sequence S = [S_AR, S_DM] and its DM order,
  *       §3 the two MoT rooms and the joint-attention equations O_AR / O_DM,
  *       §5 3D mRoPE coordinates, Δt = 6/TPS, the AR->DM time gap,
- *       §7.2 the Euler sampler update.
+ *       §6.3 the flow shift of the noise level,
+ *       §7.2 the Euler sampler update,
+ *       §12.1 the recommended steps and shift per model and mode.
  *   "NVIDIA 发布 Cosmos 3 系列四个开放权重世界模型" (four new checkpoints),
  *       section "流式生成如何工作": chunk-causal attention against a
  *       key/value cache.
@@ -181,6 +183,18 @@ mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
  * block of the next step's packed input).  n == 0 is a no-op. */
 mot_status flow_euler_step(float* x, const void* v, mot_dtype v_dt, int64_t n,
                            float sigma, float sigma_next, void* x_bf16, void* stream);
+
+/* Sampler noise levels with the flow shift (method page §6.3 shift map, §7.2
+ * sampler loop, §12.1 recommended steps and shift per mode), host only.
+ * Writes sigmas_host[k] for k = 0..n_steps into a caller-owned HOST buffer
+ * of n_steps + 1 floats: t̄ = (n_steps - k) / n_steps and
+ *     sigma_k = shift * t̄ / (1 + (shift - 1) * t̄),
+ * evaluated in double, left to right as written, and rounded once to float.
+ * sigma_0 = 1 and sigma_n = 0; shift = 1 gives sigma_k = 1 - k/n_steps.
+ * Consecutive pairs (sigma_k, sigma_k+1) are the arguments of
+ * flow_euler_step.  Errors: INVALID_ARG for n_steps < 1, a null buffer, or a
+ * shift that is not positive and finite. */
+mot_status mot_sigma_schedule(int32_t n_steps, double shift, float* sigmas_host);
 
 /* Debug/test helpers: the exact mask and the tile classes the attention
  * kernel uses.  mask_dev: device uint8 [nq][nk] (1 = allowed), nullable.

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmotattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libmotattn.so is not built; run `python -m multimodal_diffusion_transformer_amd.build` "
+        "libmotattn.so is not built; run `python multimodal_diffusion_transformer_amd/build.py` "
         "(or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -30,7 +30,7 @@ MOT_AR_CAUSAL_DM_FULL, MOT_CHUNK_CAUSAL_KV = 0, 1
 EXPORTED = [
     "mot_abi_version", "mot_status_string", "mot_build_layout", "mot_qkv_project",
     "mrope_apply", "mot_attention_fwd", "flow_euler_step", "mot_mask_materialize",
-    "mot_tile_classes_host",
+    "mot_tile_classes_host", "mot_sigma_schedule",
 ]
 
 
@@ -86,6 +86,8 @@ _lib.mot_mask_materialize.restype = ctypes.c_int
 _lib.mot_mask_materialize.argtypes = [ctypes.POINTER(mot_attn_args), _vp, _i32, _i32, _vp, _vp]
 _lib.mot_tile_classes_host.restype = ctypes.c_int
 _lib.mot_tile_classes_host.argtypes = [ctypes.POINTER(mot_attn_args), _i32, _i32, _vp]
+_lib.mot_sigma_schedule.restype = ctypes.c_int
+_lib.mot_sigma_schedule.argtypes = [_i32, ctypes.c_double, _vp]
 
 
 def _check(fn, st):
@@ -248,6 +250,16 @@ def mot_tile_classes_host(a, bm, bn):
     out = np.zeros((ntq, ntk), dtype=np.uint8)
     st = _lib.mot_tile_classes_host(ctypes.byref(a), int(bm), int(bn), out.ctypes.data_as(_vp))
     _check("mot_tile_classes_host", st)
+    return out
+
+
+def mot_sigma_schedule(n_steps, shift):
+    """Noise levels sigma_0 = 1 .. sigma_n = 0 with the flow shift, as a
+    float32 array of n_steps + 1 (host only)."""
+    n = int(n_steps)
+    out = np.zeros((max(n, 0) + 1,), dtype=np.float32)
+    st = _lib.mot_sigma_schedule(n, float(shift), out.ctypes.data_as(_vp))
+    _check("mot_sigma_schedule", st)
     return out
 
 

@@ -1,7 +1,10 @@
 """Build libmotattn.so in-tree: HIP sources for gfx950 with hipcc, the
-host layout code with g++ (-ffp-contract=off for bit-reproducible positions).
+host code (layout, noise schedule) with g++ (-ffp-contract=off, so its
+floating-point results are reproducible bit for bit).
 
-    python -m multimodal_diffusion_transformer_amd.build
+    python multimodal_diffusion_transformer_amd/build.py
+
+(run as a file: importing the package loads the library it builds).
 """
 from __future__ import annotations
 

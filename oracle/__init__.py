@@ -16,8 +16,10 @@ Sources (the pages, by title and section):
   §3 the two MoT "rooms" and the joint-attention equations O_AR / O_DM;
   §4.1 latent shapes of the video tokenizer;
   §5 the 3D mRoPE coordinates, Δt = 6/TPS and the AR→DM time gap of 15000;
-  §6.3 the rectified-flow path x_σ = σε + (1-σ)x0, v* = ε - x0;
-  §7.2 the Euler update x_next = x + (σ_next - σ)·v.
+  §6.3 the rectified-flow path x_σ = σε + (1-σ)x0, v* = ε - x0, and the
+  flow shift of the noise level;
+  §7.2 the Euler update x_next = x + (σ_next - σ)·v;
+  §12.1 the recommended steps, guidance and shift per model and mode.
 * "NVIDIA 发布 Cosmos 3 系列四个开放权重世界模型" (news page on four new
   checkpoints), section "流式生成如何工作" (how streaming generation works):
   temporal-causal chunk attention against a key/value cache.
@@ -28,4 +30,5 @@ against values the pages print, closed forms, invariants or brute force; none
 is "parity unpinned" except the end-to-end free-running chain of
 ``oracle.denoiser`` (see its docstring).
 """
-from . import layout, mask, mrope, attention, projection, euler, denoiser, streaming  # noqa: F401
+from . import (layout, mask, mrope, attention, projection, euler, denoiser, streaming,  # noqa: F401
+               schedule)

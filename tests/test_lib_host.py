@@ -9,9 +9,13 @@ import subprocess
 import numpy as np
 import pytest
 
+import json
+from fractions import Fraction
+
 import workloads as W
 from oracle import layout as olayout
 from oracle import mask as omask
+from oracle import schedule as oschedule
 
 mot = pytest.importorskip("multimodal_diffusion_transformer_amd")
 
@@ -102,6 +106,54 @@ def test_tile_counts_t2v480p_at_128():
     tc = mot.mot_tile_classes_host(a, 128, 128)
     assert tc.size == 200 * 200
     assert int((tc == omask.EMPTY).sum()) == 790 and int((tc == omask.PARTIAL).sum()) == 200
+
+
+# ---- flow-shifted noise schedule (host only) ----
+_SETTINGS = json.load(open(os.path.join(ROOT, "tests", "golden", "recommended_sampler_settings.json"),
+                           encoding="utf-8"))["settings"]
+_SCHED = sorted({(r["steps"], float(r["shift"])) for r in _SETTINGS}
+                | {(n, s) for n in (1, 2, 3, 5, 8, 13, 64) for s in (0.3, 1.0, 2.5, 3.0, 7.0, 12.5)})
+
+
+def _nearest_f32(x: Fraction) -> np.float32:
+    """The float32 nearest to the rational x (ties to even), by comparing
+    the candidates around the double nearest to x exactly."""
+    f = np.float32(float(x))
+    cands = [f, np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))]
+    def key(c):
+        bits = int(np.array(c, dtype=np.float32).view(np.uint32))
+        return (abs(Fraction(float(c)) - x), bits & 1)
+    return min(cands, key=key)
+
+
+@pytest.mark.parametrize("case", _SCHED, ids=lambda c: "n%d_s%g" % c)
+def test_sigma_schedule_bitwise_equals_oracle(case):
+    n, shift = case
+    got = mot.mot_sigma_schedule(n, shift)
+    want = np.array(oschedule.shifted_schedule(n, shift), dtype=np.float64).astype(np.float32)
+    assert got.dtype == np.float32 and got.shape == (n + 1,)
+    assert got.tobytes() == want.tobytes()
+    assert got[0] == 1.0 and got[-1] == 0.0
+
+
+@pytest.mark.parametrize("case", [c for c in _SCHED if c[0] <= 13], ids=lambda c: "n%d_s%g" % c)
+def test_sigma_schedule_is_the_nearest_float_of_the_exact_value(case):
+    n, shift = case
+    got = mot.mot_sigma_schedule(n, shift)
+    s = Fraction(shift)
+    for k in range(n + 1):
+        exact = s * (n - k) / (n + (s - 1) * (n - k))
+        assert got[k] == _nearest_f32(exact), (k, float(exact))
+
+
+def test_sigma_schedule_rejects_bad_args():
+    buf = np.zeros(8, dtype=np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    for n, shift, ptr in [(0, 5.0, p), (-3, 5.0, p), (4, 0.0, p), (4, -2.0, p),
+                          (4, float("inf"), p), (4, float("nan"), p), (4, 5.0, None)]:
+        assert mot.raw_call("mot_sigma_schedule", n, ctypes.c_double(shift), ptr) == \
+            mot.MOT_ERR_INVALID_ARG
+    assert not buf.any()
 
 
 # ---- argument checks: every one returns before any launch ----
