@@ -27,32 +27,96 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 ATTN_KERNEL = "attn_fwd_mfma"
-# sources whose text decides the attention kernel's memory traffic
-ATTN_SOURCES = ("multimodal_diffusion_transformer_amd/csrc/attention.hip",
-                "multimodal_diffusion_transformer_amd/csrc/common.hpp",
-                "multimodal_diffusion_transformer_amd/csrc/rope_dev.hpp")
+LIB_PATH = os.path.join(ROOT, "multimodal_diffusion_transformer_amd", "libmotattn.so")
 
 
-def attention_source_hash():
-    """Hash of the attention sources with comments and blank space removed,
-    so that it changes when the code does and not when its comments do."""
+def _elf_sections(elf):
+    """Section headers of a little-endian ELF64 image: dicts with name,
+    type, addr, off, size and link."""
+    import struct
+
+    if elf[:4] != b"\x7fELF" or elf[4] != 2 or elf[5] != 1:
+        raise ValueError("not a little-endian ELF64 image")
+    shoff, = struct.unpack_from("<Q", elf, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
+    secs = []
+    for i in range(shnum):
+        name, typ, _, addr, off, size, link, _, _, _ = struct.unpack_from(
+            "<IIQQQQIIQQ", elf, shoff + i * shentsize)
+        secs.append({"name": name, "type": typ, "addr": addr, "off": off, "size": size, "link": link})
+    names = secs[shstrndx]["off"]
+    for sec in secs:
+        end = elf.index(b"\0", names + sec["name"])
+        sec["name"] = elf[names + sec["name"]:end].decode()
+    return secs
+
+
+def attention_kernel_spans(so):
+    """(name, file offset, size) of every gfx950 attention kernel and kernel
+    descriptor inside the image `so` of the built library.
+
+    The library's .hip_fatbin section holds one clang offload bundle per
+    translation unit (magic, entry count, then offset / size / target
+    triple per entry); each gfx950 entry is an ELF code object whose symbol
+    table locates every kernel and its descriptor."""
+    import struct
+
+    fb = next(x for x in _elf_sections(so) if x["name"] == ".hip_fatbin")
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    spans = []
+    pos = so.find(magic, fb["off"], fb["off"] + fb["size"])
+    while pos >= 0:
+        n, = struct.unpack_from("<Q", so, pos + len(magic))
+        p = pos + len(magic) + 8
+        for _ in range(n):
+            off, size, tlen = struct.unpack_from("<QQQ", so, p)
+            triple = so[p + 24:p + 24 + tlen].decode()
+            p += 24 + tlen
+            co_off = pos + off
+            co = so[co_off:co_off + size]
+            if not triple.endswith("gfx950") or co[:4] != b"\x7fELF":
+                continue
+            secs = _elf_sections(co)
+            symtab = next(x for x in secs if x["type"] == 2)  # SHT_SYMTAB
+            strs = secs[symtab["link"]]["off"]
+            for i in range(symtab["size"] // 24):
+                st_name, _, _, shndx, value, size_ = struct.unpack_from(
+                    "<IBBHQQ", co, symtab["off"] + 24 * i)
+                name = co[strs + st_name:co.index(b"\0", strs + st_name)]
+                if ATTN_KERNEL.encode() not in name or size_ == 0 or shndx >= len(secs):
+                    continue
+                sec = secs[shndx]
+                spans.append((name, co_off + sec["off"] + value - sec["addr"], size_))
+        pos = so.find(magic, pos + len(magic), fb["off"] + fb["size"])
+    return spans
+
+
+def attention_kernel_hash(lib_path=LIB_PATH):
+    """First 16 hex digits of a sha256 over the gfx950 machine code and
+    kernel descriptors of the attention kernels in the built library, or
+    None if the library cannot be read.  It changes exactly when those
+    kernels do, and not with comments or host code."""
     import hashlib
-    import re
+    import struct
 
+    try:
+        with open(lib_path, "rb") as f:
+            so = f.read()
+        spans = attention_kernel_spans(so)
+    except (OSError, ValueError, StopIteration, struct.error, IndexError, UnicodeDecodeError):
+        return None
+    if not spans:
+        return None
     h = hashlib.sha256()
-    for rel in ATTN_SOURCES:
-        with open(os.path.join(ROOT, rel)) as f:
-            text = f.read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", "", text)
-        h.update(" ".join(text.split()).encode())
+    for name, off, size in sorted(spans):
+        h.update(name + b"\0" + struct.pack("<Q", size) + so[off:off + size])
     return h.hexdigest()[:16]
 
 
 def traffic_from_profile(workload):
     """HBM bytes per attention launch as recorded in profiles/ by the two
     counter runs (FETCH_SIZE, WRITE_SIZE) and their copy calibration, or None
-    when the attention sources changed after the counters were taken."""
+    when the attention kernels changed after the counters were taken."""
     path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.txt" % (ATTN_KERNEL, workload))
     if not os.path.exists(path):
         return None
@@ -62,7 +126,8 @@ def traffic_from_profile(workload):
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("attention_source_hash") != attention_source_hash():
+    h = attention_kernel_hash()
+    if h is None or kv.get("attention_kernel_hash") != h:
         return None
     try:
         return int(float(kv["traffic_bytes_per_launch"]))
@@ -394,7 +459,7 @@ def write_profiles(d, workload):
     cmd_head = ("commands (run on an MI355X from the repository root; <repo> is its absolute path,\n"
                 "<out> the output folder):\n  cd /tmp && export TMPDIR=/tmp\n")
     bench = "python3 <repo>/bench.py --workload %s" % workload
-    h = attention_source_hash()
+    h = attention_kernel_hash()
     flops = "7.815 TFLOP per launch (635,963,395 allowed pairs x 24 heads x 512 flop)" \
         if workload == "t2v480p_bf16" else "see DESIGN"
     # 1. kernel durations
@@ -403,7 +468,7 @@ def write_profiles(d, workload):
            "  rocprofv3 --kernel-trace --stats --output-format csv -d <out>/prof_bench -o bench -- "
            "%s --steps 5 --warmup 2 --no-cpu-baseline\n" % bench +
            "  python3 bench.py --write-profiles <out>\n\n"
-           "attention_source_hash: %s\nattention: %s\n\n" % (h, flops) +
+           "attention_kernel_hash: %s\nattention: %s\n\n" % (h, flops) +
            rocprof_summary(os.path.join(d, "prof_bench")) + "\n")
     with open(pre + "_kernel_stats.txt", "w") as f:
         f.write(txt)
@@ -431,7 +496,7 @@ def write_profiles(d, workload):
            "  FETCH_SIZE %.1f KiB x %.5f = %.4f GB\n  WRITE_SIZE %.1f KiB x %.5f = %.4f GB\n"
            % (af, ff, fb / 1e9, aw, fw, wb / 1e9) +
            "  algorithmic bytes: Q + K + V read once, O written once = 4 x N x H x D x 2 B\n\n"
-           "attention_source_hash: %s\nfetch_bytes_per_launch: %.0f\nwrite_bytes_per_launch: %.0f\n"
+           "attention_kernel_hash: %s\nfetch_bytes_per_launch: %.0f\nwrite_bytes_per_launch: %.0f\n"
            "traffic_bytes_per_launch: %.0f\n\nraw summaries:\n" % (h, fb, wb, fb + wb) +
            "\n".join(rocprof_summary(os.path.join(d, x))
                      for x in ("pmc_fetch", "pmc_write", "pmc_copy_fetch", "pmc_copy_write")) + "\n")
@@ -447,7 +512,7 @@ def write_profiles(d, workload):
         txt = ("%s on %s: shader counters, mean per dispatch.\n\n" % (ATTN_KERNEL, workload) + cmd_head +
                "  rocprofv3 --pmc %s --output-format csv -d <out>/pmc_sq -o bench -- %s --steps 2 --warmup 1"
                " --no-cpu-baseline\n  python3 bench.py --write-profiles <out>\n\n" % (" ".join(names), bench) +
-               "attention_source_hash: %s\n\n" % h +
+               "attention_kernel_hash: %s\n\n" % h +
                "".join("  %-26s %.6g\n" % (n, vals[n]) for n in names) +
                "\nderived:\n"
                "  MFMA busy cycles per MFMA instruction: %.2f (a 32x32x16 bf16 MFMA occupies the unit 32 cycles)\n"

@@ -22,8 +22,8 @@
  *     are undefined after any status other than MOT_OK.
  *   - Device pointers are caller-owned device memory (e.g. torch tensors).
  *     The library allocates no device memory.  Its only global state is a
- *     per-kernel flag recording that the kernel's LDS size attribute was set
- *     (set once, idempotent); calls are thread-safe.  One device per
+ *     per-kernel atomic flag recording that the kernel's LDS size attribute
+ *     was set (idempotent); calls are thread-safe.  One device per
  *     process is assumed: the flag is not per device.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device calls only enqueue work on it; they never synchronize.
@@ -31,6 +31,9 @@
  *   - Strides are in elements.  Device pointers must be 16-byte aligned and
  *     strides multiples of 8 elements (bf16) / 4 elements (fp32) unless a
  *     call says otherwise.
+ *   - A device call whose launch would need more than 2^32 - 1 work-items
+ *     along one grid dimension (one HIP dispatch) returns
+ *     MOT_ERR_UNSUPPORTED; each call states its limit.
  */
 #ifndef MOTATTN_H
 #define MOTATTN_H
@@ -115,7 +118,10 @@ mot_status mot_build_layout(const mot_segment* segs, int32_t n_segs, int64_t cap
  * MFMA; a bf16 output is the round-to-nearest-even of the fp32 result.
  * fp32 inputs are computed in fp32.  Supported: in_dt == MOT_BF16 with
  * d_in % 64 == 0 and d_out % 64 == 0, or in_dt == MOT_FP32 (any sizes).
- * 0 <= n_ar <= n_rows; n_rows == 0 is a no-op.  y must not alias x or w. */
+ * 0 <= n_ar <= n_rows; n_rows == 0 is a no-op.  y must not alias x or w.
+ * Dispatch limit: bf16 uses one 256-lane workgroup per 128x128 output tile
+ * of each room (at most 2^24 - 1 tiles); fp32 uses 16x16 tiles with
+ * d_out <= 2^28 - 16. */
 mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, void* y,
                            int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
                            mot_dtype in_dt, mot_dtype out_dt, void* stream);
@@ -126,7 +132,8 @@ mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, vo
  * (x_k, x_{k+P}) by a = pos[axis(k)] * theta^(-2k/head_dim), axis = t for
  * k < sec_t, h for k < sec_t+sec_h, w otherwise.  Angles and their cos/sin
  * are evaluated in fp64, the rotation in fp32, the store rounds RNE.
- * head_dim in {64, 128}; sec_t+sec_h+sec_w == head_dim/2; all >= 0. */
+ * head_dim in {64, 128}; sec_t+sec_h+sec_w == head_dim/2; all >= 0.
+ * Dispatch limit: n_tok * head_dim/8 <= 2^32 - 256. */
 mot_status mrope_apply(void* x, mot_dtype dt, int64_t n_tok, int32_t n_heads, int32_t head_dim,
                        int64_t tok_stride, int64_t head_stride, const float* pos_thw,
                        int32_t sec_t, int32_t sec_h, int32_t sec_w, float theta, void* stream);
@@ -172,7 +179,8 @@ typedef struct {
  * MOT_ERR_UNSUPPORTED when k_pos is set (bf16 rotates Q on load only: rotate
  * K beforehand with mrope_apply, which is also the layout a key cache keeps),
  * when nk > 2^31 - 65 or nq > 2^31 - 1, or when a 64-row tile of K or V
- * spans 4 GiB or more (128 * max(k_ts, v_ts) >= 2^32). */
+ * spans 4 GiB or more (128 * max(k_ts, v_ts) >= 2^32).  Dispatch limit:
+ * bf16 2 * n_heads * (nq + 512) <= 2^32 - 1; fp32 nq <= 2^32 - 64. */
 mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
 
 /* Flow-matching Euler update (method page §7.2), in place:
@@ -200,7 +208,8 @@ mot_status mot_sigma_schedule(int32_t n_steps, double shift, float* sigmas_host)
  * kernel uses.  mask_dev: device uint8 [nq][nk] (1 = allowed), nullable.
  * tiles_dev: device uint8 [ceil(nq/bm)][ceil(nk/bn)] (0 empty, 1 partial,
  * 2 full, judged on in-range pairs), nullable.  Only the mask fields of
- * args (mask, nq, nk, q0, n_ar, n_prefix, chunk_len) are read. */
+ * args (mask, nq, nk, q0, n_ar, n_prefix, chunk_len) are read.
+ * Dispatch limit: nq * nk (mask) and the tile count each <= 2^32 - 256. */
 mot_status mot_mask_materialize(const mot_attn_args* args, uint8_t* mask_dev, int32_t bm,
                                 int32_t bn, uint8_t* tiles_dev, void* stream);
 

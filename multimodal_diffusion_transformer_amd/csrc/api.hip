@@ -12,6 +12,14 @@ hipError_t attention_f32_valu(const mot_attn_args* a, const RopeTable& rt, hipSt
 hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* y, int64_t n_rows,
                        int64_t n_ar, int64_t K, int64_t N, mot_dtype in_dt, mot_dtype out_dt,
                        hipStream_t s);
+bool region_gemm_fits(int64_t n_rows, int64_t n_ar, int64_t N, mot_dtype in_dt);
+
+// One dispatch holds at most 2^32 - 1 work-items along a grid dimension.
+// True when `units` units of `lanes` work-items each, plus `extra` more,
+// stay within that.
+static bool fits_dispatch(int64_t units, int64_t lanes, int64_t extra) {
+  return units >= 0 && units <= ((int64_t)UINT32_MAX - extra) / lanes;
+}
 
 static MaskSpec mask_of(const mot_attn_args* a) {
   MaskSpec m;
@@ -21,7 +29,7 @@ static MaskSpec mask_of(const mot_attn_args* a) {
 }
 
 static bool mask_args_ok(const mot_attn_args* a) {
-  if (a->nq < 1 || a->nk < 1 || a->q0 < 0) return false;
+  if (a->nq < 1 || a->nk < 1 || a->q0 < 0 || a->q0 > INT64_MAX - a->nq) return false;
   if (a->mask == MOT_AR_CAUSAL_DM_FULL) {
     if (a->n_ar < 0 || a->n_ar > a->nk) return false;
     if (a->nk < a->q0 + a->nq) return false;  // every query sees its diagonal
@@ -91,6 +99,13 @@ extern "C" mot_status mot_attention_fwd(const mot_attn_args* a, void* stream) {
     return MOT_ERR_UNSUPPORTED;
   // the bf16 kernel rotates Q on load only; K is rotated beforehand (mrope_apply)
   if (a->dt == MOT_BF16 && a->k_pos) return MOT_ERR_UNSUPPORTED;
+  // Dispatch size.  bf16: one workgroup per (row tile, head) with 64 lanes
+  // per 32 query rows, so 2 lanes per row and head, the last tile rounded up
+  // by fewer than 512 rows.  fp32: 64 query rows of 64 lanes per workgroup
+  // along x, heads along y.
+  if (a->dt == MOT_BF16 ? !fits_dispatch(a->nq + 512, 2 * (int64_t)a->n_heads, 0)
+                        : !fits_dispatch(a->nq, 1, 63))
+    return MOT_ERR_UNSUPPORTED;
   RopeTable rt;
   rt.sec_t = a->sec_t;
   rt.sec_th = a->sec_t + a->sec_h;
@@ -118,6 +133,7 @@ extern "C" mot_status mot_qkv_project(const void* x, const void* w_ar, const voi
   if (((uintptr_t)x | (uintptr_t)w_ar | (uintptr_t)w_dm | (uintptr_t)y) & 15) return MOT_ERR_INVALID_ARG;
   if (in_dt == MOT_BF16 && (d_in % 64 || d_out % 64)) return MOT_ERR_UNSUPPORTED;
   if (in_dt == MOT_FP32 && out_dt != MOT_FP32) return MOT_ERR_UNSUPPORTED;
+  if (!region_gemm_fits(n_rows, n_ar, d_out, in_dt)) return MOT_ERR_UNSUPPORTED;
   hipError_t e = region_gemm(x, w_ar, w_dm, y, n_rows, n_ar, d_in, d_out, in_dt, out_dt,
                              (hipStream_t)stream);
   return e == hipSuccess ? MOT_OK : MOT_ERR_HIP;
@@ -128,6 +144,13 @@ extern "C" mot_status mot_mask_materialize(const mot_attn_args* a, uint8_t* mask
   if (!a || !mask_args_ok(a)) return MOT_ERR_INVALID_ARG;
   if (tiles_dev && (bm <= 0 || bn <= 0)) return MOT_ERR_INVALID_ARG;
   MaskSpec m = mask_of(a);
+  // one lane per mask entry / tile, 256 per workgroup
+  if (mask_dev && (m.nq > INT64_MAX / m.nk || !fits_dispatch(m.nq * m.nk, 1, 255)))
+    return MOT_ERR_UNSUPPORTED;
+  if (tiles_dev) {
+    const int64_t ntq = (m.nq + bm - 1) / bm, ntk = (m.nk + bn - 1) / bn;
+    if (ntq > INT64_MAX / ntk || !fits_dispatch(ntq * ntk, 1, 255)) return MOT_ERR_UNSUPPORTED;
+  }
   hipStream_t s = (hipStream_t)stream;
   if (mask_dev) {
     int64_t n = m.nq * m.nk;

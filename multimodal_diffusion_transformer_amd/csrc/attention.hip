@@ -51,6 +51,8 @@
 //  * Grid: head is the fastest index, so with H a multiple of 8 every head
 //    stays on one XCD (workgroups go round-robin over the 8 XCDs) and shares
 //    that XCD's L2; query tiles are issued heaviest first.
+#include <atomic>
+
 #include "common.hpp"
 #include "rope_dev.hpp"
 
@@ -620,12 +622,14 @@ template <int D, bool RQ>
 static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   constexpr int W = ATTN_WAVES;
   constexpr int BYTES = Lay<D>::BYTES;
-  static bool configured = false;
-  if (!configured) {
+  // Set the LDS size attribute once; concurrent first calls may both set it
+  // (it is idempotent), and the flag itself is atomic.
+  static std::atomic<bool> configured{false};
+  if (!configured.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute((const void*)attn_fwd_mfma<D, W, RQ>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, BYTES);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured.store(true, std::memory_order_release);
   }
   dim3 grid((unsigned)(p.n_qtiles * p.n_heads));
   hipLaunchKernelGGL((attn_fwd_mfma<D, W, RQ>), grid, dim3(64 * W), BYTES, s, p);

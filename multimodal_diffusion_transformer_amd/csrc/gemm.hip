@@ -14,6 +14,8 @@
 // operand reads are conflict-free ds_read_b128.  Two LDS stages overlap the
 // next tile's global loads with the current MFMAs.
 // fp32 path: a plain LDS-tiled fp32 VALU GEMM.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace mot {
@@ -428,6 +430,18 @@ __global__ __launch_bounds__(256) void gemm_region_f32(const float* x, const flo
   if (row < M && col < N) y[row * N + col] = acc;
 }
 
+// Whether one dispatch (at most 2^32 - 1 work-items along a grid dimension)
+// covers the problem: fp32 launches FT x FT output tiles of 256 lanes on a
+// 2D grid; bf16 launches one GM x GN tile of 256 lanes per workgroup for
+// each room's rows (the direct-to-LDS kernel's tiles are larger).
+bool region_gemm_fits(int64_t n_rows, int64_t n_ar, int64_t N, mot_dtype in_dt) {
+  const int64_t lim = (int64_t)UINT32_MAX;
+  if (in_dt == MOT_FP32) return (N + FT - 1) / FT <= lim / 256 && (n_rows + FT - 1) / FT <= lim;
+  const int64_t tiles_m = (n_ar + GM - 1) / GM + (n_rows - n_ar + GM - 1) / GM;
+  const int64_t tiles_n = (N + GN - 1) / GN;
+  return tiles_n <= lim / 256 && tiles_m <= lim / 256 / tiles_n;
+}
+
 hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* y, int64_t n_rows,
                        int64_t n_ar, int64_t K, int64_t N, mot_dtype in_dt, mot_dtype out_dt,
                        hipStream_t s) {
@@ -453,12 +467,12 @@ hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* 
     p.tiles_n = (int)((N + HN - 1) / HN);
     const int64_t blocks = (int64_t)(p.tiles_m[0] + p.tiles_m[1]) * p.tiles_n;
     if (blocks == 0) return hipSuccess;
-    static bool configured_dma[2] = {false, false};
+    static std::atomic<bool> configured_dma[2] = {{false}, {false}};
     const void* fn = ob ? (const void*)gemm_region_mfma<true> : (const void*)gemm_region_mfma<false>;
-    if (!configured_dma[ob]) {
+    if (!configured_dma[ob].load(std::memory_order_acquire)) {
       hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, H_SMEM_BYTES);
       if (e != hipSuccess) return e;
-      configured_dma[ob] = true;
+      configured_dma[ob].store(true, std::memory_order_release);
     }
     if (ob)
       hipLaunchKernelGGL(gemm_region_mfma<true>, dim3((unsigned)blocks), dim3(256), H_SMEM_BYTES, s, p);
@@ -472,13 +486,15 @@ hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* 
   p.tiles_n = (int)((N + GN - 1) / GN);
   const int64_t blocks = (int64_t)(p.tiles_m[0] + p.tiles_m[1]) * p.tiles_n;
   if (blocks == 0) return hipSuccess;
-  static bool configured[2] = {false, false};
+  // Set the LDS size attribute once; concurrent first calls may both set it
+  // (it is idempotent), and the flag itself is atomic.
+  static std::atomic<bool> configured[2] = {{false}, {false}};
   const int ob = out_dt == MOT_BF16 ? 1 : 0;
   const void* fn = ob ? (const void*)gemm_region_bf16<true> : (const void*)gemm_region_bf16<false>;
-  if (!configured[ob]) {
+  if (!configured[ob].load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, G_SMEM_BYTES);
     if (e != hipSuccess) return e;
-    configured[ob] = true;
+    configured[ob].store(true, std::memory_order_release);
   }
   if (ob)
     hipLaunchKernelGGL(gemm_region_bf16<true>, dim3((unsigned)blocks), dim3(256), G_SMEM_BYTES, s, p);

@@ -106,6 +106,9 @@ extern "C" mot_status mrope_apply(void* x, mot_dtype dt, int64_t n_tok, int32_t 
   if (((uintptr_t)x & 15) || ((uintptr_t)pos_thw & 3)) return MOT_ERR_INVALID_ARG;
   if (tok_stride % align || head_stride % align || tok_stride <= 0 || head_stride <= 0)
     return MOT_ERR_INVALID_ARG;
+  // head_dim/8 lanes per token, 256 per workgroup, within one dispatch's
+  // 2^32 - 1 work-items
+  if (n_tok > ((int64_t)UINT32_MAX - 255) / (head_dim / 8)) return MOT_ERR_UNSUPPORTED;
   RopeFreqs fr;
   for (int k = 0; k < head_dim / 2; ++k) fr.inv_freq[k] = pow((double)theta, -2.0 * k / head_dim);
   const int sec_th = sec_t + sec_h;

@@ -29,24 +29,43 @@ def test_480p_flops_per_launch():
     assert abs(4.0 * wl.head_dim * wl.n_heads * pairs - 7.815e12) < 1e9
 
 
-def test_traffic_is_read_only_for_the_profiled_sources(monkeypatch):
+def test_traffic_is_read_only_for_the_profiled_kernels(monkeypatch):
     rec = bench.traffic_from_profile("t2v480p_bf16")
     assert rec is not None and rec > 0.6e9  # at least Q, K, V read and O written once
-    monkeypatch.setattr(bench, "attention_source_hash", lambda: "0" * 16)
+    monkeypatch.setattr(bench, "attention_kernel_hash", lambda: "0" * 16)
+    assert bench.traffic_from_profile("t2v480p_bf16") is None
+    monkeypatch.setattr(bench, "attention_kernel_hash", lambda: None)
     assert bench.traffic_from_profile("t2v480p_bf16") is None
     assert bench.traffic_from_profile("no_such_workload") is None
 
 
-def test_source_hash_ignores_comments(tmp_path, monkeypatch):
-    a = tmp_path / "a.hip"
-    a.write_text("int f() { return 1; }  // one\n/* block\ncomment */\n")
-    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "ATTN_SOURCES", ("a.hip",))
-    h1 = bench.attention_source_hash()
-    a.write_text("int f() {\n  return 1;\n}  // another comment\n")
-    assert bench.attention_source_hash() == h1
-    a.write_text("int f() { return 2; }\n")
-    assert bench.attention_source_hash() != h1
+def test_kernel_hash_tracks_the_attention_machine_code(tmp_path):
+    so = open(bench.LIB_PATH, "rb").read()
+    spans = bench.attention_kernel_spans(so)
+    names = {n for n, _, _ in spans}
+    # bf16 kernel at D = 128 and 64, with and without Q rotation, and descriptors
+    assert len(spans) == 8 and sum(n.endswith(b".kd") for n in names) == 4
+    assert all(size > 0 for _, _, size in spans)
+    h0 = bench.attention_kernel_hash()
+    assert h0 is not None and len(h0) == 16
+
+    def flipped(off):
+        b = bytearray(so)
+        b[off] ^= 0x01
+        p = tmp_path / ("lib_%d.so" % off)
+        p.write_bytes(bytes(b))
+        return bench.attention_kernel_hash(str(p))
+
+    # a bit inside the first attention kernel changes the hash
+    _, off, size = sorted(spans)[0]
+    assert flipped(off + size // 2) != h0
+    # a bit of host code (the ELF .text of the library) does not
+    text = next(x for x in bench._elf_sections(so) if x["name"] == ".text")
+    assert flipped(text["off"] + text["size"] // 2) == h0
+    # an unreadable library gives no hash
+    (tmp_path / "junk.so").write_bytes(b"not an elf")
+    assert bench.attention_kernel_hash(str(tmp_path / "junk.so")) is None
+    assert bench.attention_kernel_hash(str(tmp_path / "missing.so")) is None
 
 
 def test_rocprof_summaries_parse_csv(tmp_path):

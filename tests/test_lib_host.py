@@ -194,6 +194,37 @@ def test_attention_bf16_unsupported(kw):
     assert st == mot.MOT_ERR_UNSUPPORTED
 
 
+def test_launches_past_one_dispatch_are_unsupported():
+    # Sizes whose grid would exceed 2^32 - 1 work-items: every call returns
+    # UNSUPPORTED before any launch (the pointers are never dereferenced).
+    vp = ctypes.c_void_p
+    # bf16 attention: chunk mode lets nq exceed nk; 2 * 4 heads * (2^30 + 512) > 2^32
+    a = _args(mask=mot.MOT_CHUNK_CAUSAL_KV, chunk_len=64, nq=1 << 30, nk=64, n_heads=4)
+    assert mot.raw_call("mot_attention_fwd", ctypes.byref(a), None) == mot.MOT_ERR_UNSUPPORTED
+    a = _args(mask=mot.MOT_CHUNK_CAUSAL_KV, chunk_len=64, nq=1 << 32, nk=64, n_heads=1,
+              dt=mot.MOT_FP32)
+    assert mot.raw_call("mot_attention_fwd", ctypes.byref(a), None) == mot.MOT_ERR_UNSUPPORTED
+    # mRoPE: 2^29 tokens x 16 lanes
+    assert mot.raw_call("mrope_apply", vp(4096), 0, 1 << 29, 1, 128, 1024, 128, vp(4096), 16, 24,
+                        24, ctypes.c_float(1e4), None) == mot.MOT_ERR_UNSUPPORTED
+    # projection: 2^31 rows x 2^16 columns of 128 x 128 tiles; fp32 d_out = 2^28
+    assert mot.raw_call("mot_qkv_project", vp(4096), vp(4096), vp(4096), vp(4096), 1 << 31, 0, 64,
+                        1 << 16, 0, 0, None) == mot.MOT_ERR_UNSUPPORTED
+    assert mot.raw_call("mot_qkv_project", vp(4096), vp(4096), vp(4096), vp(4096), 16, 0, 4,
+                        1 << 28, 1, 1, None) == mot.MOT_ERR_UNSUPPORTED
+    # mask of the long 480p sequence: 76,954^2 entries > 2^32
+    m = mot.mask_args(76954, 76954, 0, W.AR_CAUSAL_DM_FULL, n_ar=514)
+    assert mot.raw_call("mot_mask_materialize", ctypes.byref(m), vp(4096), 128, 64, None,
+                        None) == mot.MOT_ERR_UNSUPPORTED
+    # tile classes at 1 x 1 tiles of the same sequence
+    assert mot.raw_call("mot_mask_materialize", ctypes.byref(m), None, 1, 1, vp(4096),
+                        None) == mot.MOT_ERR_UNSUPPORTED
+    # q0 + nq past int64 is rejected, not wrapped
+    m = mot.mask_args(1 << 62, 64, (1 << 63) - 2, W.AR_CAUSAL_DM_FULL)
+    assert mot.raw_call("mot_mask_materialize", ctypes.byref(m), vp(4096), 128, 64, None,
+                        None) == mot.MOT_ERR_INVALID_ARG
+
+
 def test_projection_and_rope_and_euler_reject_bad_args():
     vp = ctypes.c_void_p
     # projection: n_ar > n_rows; unaligned; bf16 with d_in not a multiple of 64
