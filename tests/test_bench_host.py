@@ -88,3 +88,13 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_cpu_baseline_reports_a_bounded_oracle_sample():
+    wl = W.BY_NAME["tiny_fp32"]
+    cb = bench.cpu_baseline(wl, budget_s=0.5)
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["cores"] >= 1
+    assert cb["value"] > 0
+    n_ar = W.region_counts(wl.segments)[0]
+    # every DM row of every head, as the tiny workload fits the budget
+    assert "%d DM query rows" % ((wl.n_tokens - n_ar) * wl.n_heads) in cb["sample"]
