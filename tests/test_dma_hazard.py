@@ -18,9 +18,9 @@ WINDOW = 8     # instructions looked back from each copy
 WAIT_STATES = 5  # required between a VALU write of an SGPR and a vector-memory read of it
 
 
-def _kernels(tmp_path):
+def _kernels(tmp_path, lib=LIB):
     fb = tmp_path / "fatbin"
-    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section", ".hip_fatbin=%s" % fb, LIB],
+    subprocess.run([os.path.join(LLVM, "llvm-objcopy"), "--dump-section", ".hip_fatbin=%s" % fb, lib],
                    check=True)
     data = fb.read_bytes()
     starts = [m.start() for m in re.finditer(re.escape(b"__CLANG_OFFLOAD_BUNDLE__"), data)]
@@ -47,12 +47,10 @@ def _kernels(tmp_path):
     return out
 
 
-@pytest.mark.skipif(not os.path.exists(LIB) or not os.path.exists(os.path.join(LLVM, "llvm-objdump")),
-                    reason="library not built or ROCm LLVM tools missing")
-def test_no_lds_dma_reads_a_vector_written_base(tmp_path):
-    kernels = _kernels(tmp_path)
-    assert any("attn_fwd_mfma" in k for k in kernels), "attention kernels not found in the build"
-    copies = bad = 0
+def _hazards(kernels):
+    """(copies, list of copies whose base a v_readfirstlane wrote with fewer
+    than WAIT_STATES wait states in between)."""
+    copies = 0
     report = []
     for name, ins in kernels.items():
         for i, line in enumerate(ins):
@@ -66,10 +64,43 @@ def test_no_lds_dma_reads_a_vector_written_base(tmp_path):
                 w = re.search(r"v_readfirstlane_b32\s+s(\d+),", prev)
                 if w and w.group(1) in regs:
                     if waits < WAIT_STATES:
-                        bad += 1
                         report.append("%s: %s" % (name[:60], line))
                     break
                 n = re.search(r"s_nop\s+(0x[0-9a-f]+|\d+)", prev)
                 waits += int(n.group(1), 0) + 1 if n else 1
+    return copies, report
+
+
+_TOOLS = os.path.exists(os.path.join(LLVM, "llvm-objdump"))
+
+
+@pytest.mark.skipif(not os.path.exists(LIB) or not _TOOLS,
+                    reason="library not built or ROCm LLVM tools missing")
+def test_no_lds_dma_reads_a_vector_written_base(tmp_path):
+    kernels = _kernels(tmp_path)
+    assert any("attn_fwd_mfma" in k for k in kernels), "attention kernels not found in the build"
+    copies, report = _hazards(kernels)
     assert copies > 0, "no LDS-DMA copies found"
-    assert bad == 0, "copies with a VALU-written base:\n" + "\n".join(report[:10])
+    assert not report, "copies with a VALU-written base:\n" + "\n".join(report[:10])
+
+
+@pytest.mark.skipif(not _TOOLS or not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="ROCm compiler or LLVM tools missing")
+def test_switched_off_direct_to_lds_gemm_keeps_its_wait_states(tmp_path):
+    # The direct-to-LDS projection GEMM is compiled only on request
+    # (-DMOT_GEMM_DMA=1).  Its VALU-computed bases need the wait states its
+    # copy helper inserts; check that build too.
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_motattn_build", os.path.join(ROOT, "multimodal_diffusion_transformer_amd", "build.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    obj = tmp_path / "gemm_dma.o"
+    subprocess.run(["/opt/rocm/bin/hipcc", *b.HIP_FLAGS, "-DMOT_GEMM_DMA=1", "-c",
+                    os.path.join(b.CSRC, "gemm.hip"), "-o", str(obj)], check=True,
+                   capture_output=True)
+    kernels = _kernels(tmp_path, str(obj))
+    assert any("gemm_region_mfma" in k for k in kernels), "direct-to-LDS GEMM not in that build"
+    copies, report = _hazards({k: v for k, v in kernels.items() if "gemm_region_mfma" in k})
+    assert copies > 0, "no LDS-DMA copies found"
+    assert not report, "copies with a VALU-written base:\n" + "\n".join(report[:10])
