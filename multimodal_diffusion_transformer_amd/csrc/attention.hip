@@ -126,14 +126,17 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // each LDS read (it cannot tell that the copies target another stage); the
 // kernel waits on vmcnt itself.  The instruction has no VGPR result.
 //
-// Hazard: the hardware needs wait states between a VALU write of an SGPR and
-// a vector-memory instruction reading it, and the compiler inserts none in
-// front of inline asm.  The base must therefore reach the SGPR pair through
-// scalar instructions (as every tile base here does: it is built from
-// kernel arguments and wave-uniform loop counters); a base that only exists
-// in VGPRs, moved over by v_readfirstlane right before the copy, makes the
-// copy read a stale base.  A host test scans the built library for that
-// pattern.
+// Hazards: the compiler inserts no wait states in front of inline asm.
+//  * A VALU write of an SGPR needs 5 before a vector-memory instruction reads
+//    it.  The base must therefore reach the SGPR pair through scalar
+//    instructions (as every tile base here does: it is built from kernel
+//    arguments and wave-uniform loop counters); a base that only exists in
+//    VGPRs, moved over by v_readfirstlane right before the copy, makes the
+//    copy read a stale base.
+//  * A scalar write of M0 (the LDS destination, set by the "{m0}"
+//    constraint just before the asm) needs 1 before an LDS-DMA copy reads
+//    it; the asm starts with s_nop 0 for that.
+// A host test scans the built library for both patterns.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds) {
   // the tile base is wave-uniform by construction; make it an SGPR pair
   // (readfirstlane returns int: go through uint32_t so nothing sign-extends)
@@ -141,7 +144,7 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "{m0}"(lds) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

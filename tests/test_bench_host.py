@@ -29,7 +29,18 @@ def test_480p_flops_per_launch():
     assert abs(4.0 * wl.head_dim * wl.n_heads * pairs - 7.815e12) < 1e9
 
 
+def _recorded_hash(workload):
+    path = os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.txt" % (bench.ATTN_KERNEL, workload))
+    for line in open(path):
+        if line.startswith("attention_kernel_hash:"):
+            return line.split(":", 1)[1].strip()
+    return None
+
+
 def test_traffic_is_read_only_for_the_profiled_kernels(monkeypatch):
+    h = _recorded_hash("t2v480p_bf16")
+    assert h is not None and len(h) == 16
+    monkeypatch.setattr(bench, "attention_kernel_hash", lambda: h)
     rec = bench.traffic_from_profile("t2v480p_bf16")
     assert rec is not None and rec > 0.6e9  # at least Q, K, V read and O written once
     monkeypatch.setattr(bench, "attention_kernel_hash", lambda: "0" * 16)

@@ -1,9 +1,13 @@
-"""Host-side check of the built library's gfx950 machine code: no LDS-DMA
-copy (global_load_lds_*) may take its scalar base from an SGPR pair that a
-vector instruction (v_readfirstlane) wrote just before.  The hardware needs
-wait states between a VALU write of an SGPR and a vector-memory read of it,
-and the compiler inserts none in front of the inline asm that issues these
-copies; a stale base makes the copy read from a wrong address."""
+"""Host-side check of the built library's gfx950 machine code around every
+LDS-DMA copy (global_load_lds_*), which the kernels issue from inline asm;
+the compiler inserts no wait states in front of inline asm.
+
+* No copy may take its scalar base from an SGPR pair that a vector
+  instruction (v_readfirstlane) wrote fewer than 5 wait states before: a
+  stale base makes the copy read from a wrong address.
+* No copy may follow a scalar write of M0, its LDS destination, with fewer
+  than 1 wait state in between.  The compiler keeps that distance for the
+  copies it emits itself on gfx950 (an s_nop 0 between the two)."""
 import os
 import re
 import shutil
@@ -16,6 +20,7 @@ LIB = os.path.join(ROOT, "multimodal_diffusion_transformer_amd", "libmotattn.so"
 LLVM = "/opt/rocm/llvm/bin"
 WINDOW = 8     # instructions looked back from each copy
 WAIT_STATES = 5  # required between a VALU write of an SGPR and a vector-memory read of it
+M0_WAIT_STATES = 1  # required between a scalar write of M0 and an LDS-DMA copy
 
 
 def _kernels(tmp_path, lib=LIB):
@@ -47,6 +52,12 @@ def _kernels(tmp_path, lib=LIB):
     return out
 
 
+def _waits(prev):
+    """Wait states one instruction provides."""
+    n = re.search(r"s_nop\s+(0x[0-9a-f]+|\d+)", prev)
+    return int(n.group(1), 0) + 1 if n else 1
+
+
 def _hazards(kernels):
     """(copies, list of copies whose base a v_readfirstlane wrote with fewer
     than WAIT_STATES wait states in between)."""
@@ -66,8 +77,29 @@ def _hazards(kernels):
                     if waits < WAIT_STATES:
                         report.append("%s: %s" % (name[:60], line))
                     break
-                n = re.search(r"s_nop\s+(0x[0-9a-f]+|\d+)", prev)
-                waits += int(n.group(1), 0) + 1 if n else 1
+                waits += _waits(prev)
+    return copies, report
+
+
+def _m0_hazards(kernels):
+    """(copies, list of copies that follow a scalar write of M0 with fewer
+    than M0_WAIT_STATES wait states in between)."""
+    copies = 0
+    report = []
+    for name, ins in kernels.items():
+        for i, line in enumerate(ins):
+            if not re.search(r"global_load_lds_dword", line):
+                continue
+            copies += 1
+            waits = 0
+            for prev in reversed(ins[max(0, i - WINDOW):i]):
+                if re.match(r"s_\w+\s+m0,", prev):
+                    if waits < M0_WAIT_STATES:
+                        report.append("%s: %s" % (name[:60], line))
+                    break
+                waits += _waits(prev)
+                if waits >= M0_WAIT_STATES:
+                    break
     return copies, report
 
 
@@ -82,6 +114,8 @@ def test_no_lds_dma_reads_a_vector_written_base(tmp_path):
     copies, report = _hazards(kernels)
     assert copies > 0, "no LDS-DMA copies found"
     assert not report, "copies with a VALU-written base:\n" + "\n".join(report[:10])
+    copies, report = _m0_hazards(kernels)
+    assert not report, "copies right after an M0 write:\n" + "\n".join(report[:10])
 
 
 @pytest.mark.skipif(not _TOOLS or not os.path.exists("/opt/rocm/bin/hipcc"),
@@ -101,6 +135,9 @@ def test_switched_off_direct_to_lds_gemm_keeps_its_wait_states(tmp_path):
                    capture_output=True)
     kernels = _kernels(tmp_path, str(obj))
     assert any("gemm_region_mfma" in k for k in kernels), "direct-to-LDS GEMM not in that build"
-    copies, report = _hazards({k: v for k, v in kernels.items() if "gemm_region_mfma" in k})
+    gemm = {k: v for k, v in kernels.items() if "gemm_region_mfma" in k}
+    copies, report = _hazards(gemm)
     assert copies > 0, "no LDS-DMA copies found"
     assert not report, "copies with a VALU-written base:\n" + "\n".join(report[:10])
+    copies, report = _m0_hazards(gemm)
+    assert not report, "copies right after an M0 write:\n" + "\n".join(report[:10])
