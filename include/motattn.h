@@ -133,7 +133,7 @@ mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, vo
  * k < sec_t, h for k < sec_t+sec_h, w otherwise.  Angles and their cos/sin
  * are evaluated in fp64, the rotation in fp32, the store rounds RNE.
  * head_dim in {64, 128}; sec_t+sec_h+sec_w == head_dim/2; all >= 0.
- * Dispatch limit: n_tok * head_dim/8 <= 2^32 - 256. */
+ * n_tok == 0 is a no-op.  Dispatch limit: n_tok * head_dim/8 <= 2^32 - 256. */
 mot_status mrope_apply(void* x, mot_dtype dt, int64_t n_tok, int32_t n_heads, int32_t head_dim,
                        int64_t tok_stride, int64_t head_stride, const float* pos_thw,
                        int32_t sec_t, int32_t sec_h, int32_t sec_w, float theta, void* stream);

@@ -246,3 +246,8 @@ def test_projection_and_rope_and_euler_reject_bad_args():
                         ctypes.c_float(0.5), None, None) == mot.MOT_ERR_INVALID_ARG
     assert mot.raw_call("flow_euler_step", None, None, 0, 0, ctypes.c_float(1.0),
                         ctypes.c_float(0.5), None, None) == mot.MOT_OK
+    # empty projection and rope are no-ops that touch nothing (null pointers allowed)
+    assert mot.raw_call("mot_qkv_project", None, None, None, None, 0, 0, 64, 64, 0, 0,
+                        None) == mot.MOT_OK
+    assert mot.raw_call("mrope_apply", None, 0, 0, 2, 128, 256, 128, None, 16, 24, 24,
+                        ctypes.c_float(1e4), None) == mot.MOT_OK
