@@ -141,12 +141,13 @@ def _build() -> List[Workload]:
                   video(DM_NOISY, 2, 3, 12, 20), action(DM_NOISY, 32)),
         sigmas=_linear(10)))
     # 3. Text-to-video 480p-shaped: 512 text + EOS + BOG; 16 noisy latent
-    #    frames on a 30x52 grid (24,960 tokens); no clean block.
+    #    frames on a 30x52 grid (24,960 tokens); no clean block.  The
+    #    benchmark times one step, the first of a 40-step linear schedule.
     w.append(Workload(
         wid=2, name="t2v480p_bf16", dtype="bf16", n_heads=24, head_dim=128,
         hidden=3072, sections=(16, 24, 24),
         segments=(text(512), *eos_bog(), video(DM_NOISY, 16, 1, 30, 52)),
-        sigmas=(1.0, 0.9)))
+        sigmas=(1.0, 0.975)))
     # 4. Streaming chunk attention (Sim-Auto-shaped): 6 views at 12x20 per
     #    latent frame; cache = 256 text + EOS + BOG and 8 history frames;
     #    each query chunk is one latent frame; 4 steps per chunk, 16 chunks.
@@ -166,7 +167,7 @@ def _build() -> List[Workload]:
         head_dim=128, hidden=3072, sections=(16, 24, 24),
         segments=(text(512), *eos_bog(), video(DM_CLEAN, 1, 1, 30, 52),
                   video(DM_NOISY, 48, 1, 30, 52)),
-        sigmas=(1.0, 0.9)))
+        sigmas=(1.0, 0.975)))
     return w
 
 
