@@ -1,0 +1,120 @@
+"""The boundary is usable from plain C (CPU only).
+
+The header compiles as strict C99 and as C++, and a C program linked against
+libmotattn.so calls the host-only entry points (version, status strings,
+layout of the tiny workload, flow-shifted noise schedule, tile classes);
+its output must equal the oracle's.  No device work is launched.
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import layout as olayout
+from oracle import mask as omask
+from oracle import schedule as oschedule
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INC = os.path.join(ROOT, "include")
+LIBDIR = os.path.join(ROOT, "multimodal_diffusion_transformer_amd")
+
+pytestmark = pytest.mark.skipif(
+    shutil.which("gcc") is None or not os.path.exists(os.path.join(LIBDIR, "libmotattn.so")),
+    reason="gcc or the built library missing")
+
+PROGRAM = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#include "motattn.h"
+
+int main(void) {
+  /* the tiny workload: 32 text + EOS + BOG | clean 1x4x6 video | noisy 2x4x6 video + 8 actions */
+  mot_segment s[6];
+  int i;
+  int64_t n = 0, n_ar = 0, k;
+  float* pos;
+  uint8_t* reg;
+  float sig[5];
+  mot_attn_args a;
+  uint8_t tiles[4];
+  mot_status st;
+  for (i = 0; i < 6; ++i) {
+    s[i].region = 0; s[i].kind = 0; s[i].n_tokens = 0; s[i].n_frames = 0; s[i].n_views = 1;
+    s[i].grid_h = 0; s[i].grid_w = 0; s[i].rate = 0.0; s[i].frame0 = -1; s[i].step0 = 0;
+  }
+  s[0].region = MOT_REGION_AR; s[0].kind = MOT_KIND_TEXT; s[0].n_tokens = 32;
+  s[1].region = MOT_REGION_AR; s[1].kind = MOT_KIND_SPECIAL; s[1].n_tokens = 1;
+  s[2].region = MOT_REGION_AR; s[2].kind = MOT_KIND_SPECIAL; s[2].n_tokens = 1;
+  s[3].region = MOT_REGION_DM_CLEAN; s[3].kind = MOT_KIND_VIDEO; s[3].n_frames = 1;
+  s[3].grid_h = 4; s[3].grid_w = 6; s[3].rate = 24.0;
+  s[4].region = MOT_REGION_DM_NOISY; s[4].kind = MOT_KIND_VIDEO; s[4].n_frames = 2;
+  s[4].grid_h = 4; s[4].grid_w = 6; s[4].rate = 24.0;
+  s[5].region = MOT_REGION_DM_NOISY; s[5].kind = MOT_KIND_ACTION; s[5].n_tokens = 8;
+  s[5].rate = 15.0;
+
+  printf("abi %d\n", mot_abi_version());
+  printf("status1 %s\n", mot_status_string(MOT_ERR_INVALID_ARG));
+  st = mot_build_layout(s, 6, 0, &n, &n_ar, NULL, NULL);  /* sizing call */
+  if (st != MOT_ERR_INVALID_ARG || n <= 0) return 2;
+  pos = (float*)malloc(sizeof(float) * 3 * (size_t)n);
+  reg = (uint8_t*)malloc((size_t)n);
+  st = mot_build_layout(s, 6, n, &n, &n_ar, pos, reg);
+  if (st != MOT_OK) return 3;
+  printf("layout %lld %lld\n", (long long)n, (long long)n_ar);
+  for (k = 0; k < n; ++k) printf("p %d %.9g %.9g %.9g\n", reg[k], pos[3 * k], pos[3 * k + 1], pos[3 * k + 2]);
+  if (mot_sigma_schedule(4, 5.0, sig) != MOT_OK) return 4;
+  printf("sigma %.9g %.9g %.9g %.9g %.9g\n", sig[0], sig[1], sig[2], sig[3], sig[4]);
+  memset(&a, 0, sizeof a);
+  a.mask = MOT_AR_CAUSAL_DM_FULL; a.nq = 114; a.nk = 114; a.q0 = 0; a.n_ar = 34;
+  a.n_prefix = 0; a.chunk_len = 0;
+  if (mot_tile_classes_host(&a, 64, 64, tiles) != MOT_OK) return 5;
+  printf("tiles %d %d %d %d\n", tiles[0], tiles[1], tiles[2], tiles[3]);
+  free(pos);
+  free(reg);
+  return 0;
+}
+"""
+
+
+def test_header_is_strict_c99_and_cpp(tmp_path):
+    src = tmp_path / "h.c"
+    src.write_text('#include "motattn.h"\nint main(void) { return mot_abi_version() == 1 ? 0 : 1; }\n')
+    for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++11")):
+        r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                            "-I", INC] + (["-x", "c++"] if cc == "g++" else []) + [str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, (cc, r.stderr)
+
+
+def test_c_program_matches_the_oracle(tmp_path):
+    src, exe = tmp_path / "use.c", tmp_path / "use"
+    src.write_text(PROGRAM)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", INC, str(src), "-o", str(exe),
+                        "-L", LIBDIR, "-lmotattn", "-Wl,-rpath," + LIBDIR],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, (out.returncode, out.stderr)
+    lines = out.stdout.splitlines()
+    assert lines[0] == "abi 1" and lines[1] == "status1 invalid argument"
+
+    wl = W.BY_NAME["tiny_fp32"]
+    pos, reg, n_ar = olayout.build(wl.segments)
+    assert lines[2] == "layout %d %d" % (len(reg), n_ar)
+    got = [l.split() for l in lines[3:3 + len(reg)]]
+    assert [int(g[1]) for g in got] == [int(x) for x in reg]
+    # %.9g round-trips float32 exactly
+    np.testing.assert_array_equal(np.array([[float(x) for x in g[2:]] for g in got], np.float32),
+                                  np.asarray(pos, np.float32))
+
+    sig = [float(x) for x in lines[3 + len(reg)].split()[1:]]
+    want = np.array(oschedule.shifted_schedule(4, 5.0), np.float64).astype(np.float32)
+    np.testing.assert_array_equal(np.array(sig, np.float32), want)
+
+    tiles = [int(x) for x in lines[4 + len(reg)].split()[1:]]
+    m = omask.materialize(114, 114, 0, W.AR_CAUSAL_DM_FULL, 34, 0, 1)
+    assert tiles == [int(x) for x in omask.tile_classes(m, 64, 64).ravel()]
