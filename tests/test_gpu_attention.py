@@ -93,9 +93,10 @@ def test_attention_fp32_tiny_workload_full():
 @pytest.mark.parametrize("rope_k", [False, True])
 def test_attention_fused_rope_on_load(dtype, d, rope_k):
     if rope_k and dtype == "bf16":
-        pytest.skip("bf16 rotates Q on load only: a GPU memory fault in the bf16 kernel variant that "
-                    "also rotated K on load had no cause found, so that variant was removed and the "
-                    "library rejects k_pos for bf16 (checked on the host)")
+        pytest.skip("bf16 rotates Q on load only: the bf16 kernel variant that also rotated K on "
+                    "load faulted the GPU (its tile copies read a base register that a vector "
+                    "instruction had just written, with no wait states); the variant was removed "
+                    "and the library rejects k_pos for bf16 (checked on the host)")
     dev = device()
     mot = _mot()
     wl = W.BY_NAME["policy_bf16"]
