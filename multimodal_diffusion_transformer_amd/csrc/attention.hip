@@ -10,8 +10,8 @@
 //    v_mfma_f32_32x32x16_bf16.  In the 32x32 accumulator layout a lane owns
 //    one column, so every lane owns ONE query and 16 of its keys per
 //    32-key block; row statistics are per-lane scalars and the only
-//    cross-lane step (a permlane32 swap) runs on a row's first tile and when
-//    a reference max moves.
+//    cross-lane step (a permlane32 swap) runs on a row's first tile, when a
+//    reference max moves, and once at the end for the row sums.
 //  * K rows are fed to the MFMA in a permuted order so that lane half g
 //    ends up holding keys 16g..16g+15 of each 32-key block in register
 //    order.  Those registers, packed to bf16, are exactly the B operand of
