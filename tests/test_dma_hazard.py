@@ -141,3 +141,33 @@ def test_switched_off_direct_to_lds_gemm_keeps_its_wait_states(tmp_path):
     assert not report, "copies with a VALU-written base:\n" + "\n".join(report[:10])
     copies, report = _m0_hazards(gemm)
     assert not report, "copies right after an M0 write:\n" + "\n".join(report[:10])
+
+
+@pytest.mark.skipif(not _TOOLS or not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="ROCm compiler or LLVM tools missing")
+def test_compiler_keeps_a_wait_state_between_m0_and_its_own_copies(tmp_path):
+    # The rule the copy helpers follow by hand: for LDS-DMA copies it emits
+    # itself on gfx950, the compiler never lets a copy directly follow the
+    # scalar write of its M0.  Compile two copies from the builtin and check.
+    src = tmp_path / "probe.hip"
+    src.write_text(
+        "#include <hip/hip_runtime.h>\n"
+        "__global__ void probe(const int* __restrict__ g, int off) {\n"
+        "  extern __shared__ int lds[];\n"
+        "  __builtin_amdgcn_global_load_lds(g + threadIdx.x,\n"
+        "      (__attribute__((address_space(3))) void*)(lds + off), 4, 0, 0);\n"
+        "  __builtin_amdgcn_global_load_lds(g + 64 + threadIdx.x,\n"
+        "      (__attribute__((address_space(3))) void*)(lds + off + 256), 4, 0, 0);\n"
+        "}\n")
+    asm = tmp_path / "probe.s"
+    subprocess.run(["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O3", "--cuda-device-only", "-S",
+                    str(src), "-o", str(asm)], check=True, capture_output=True)
+    ins = [l.strip() for l in asm.read_text().splitlines()
+           if l.startswith("\t") and not l.strip().startswith((".", ";"))]
+    kernels = {"probe": ins}
+    copies, report = _m0_hazards(kernels)
+    assert copies == 2
+    assert not report, report
+    # and at least one of them needed the compiler's own s_nop to get there
+    assert any(ins[i - 1].startswith("s_nop") and re.match(r"s_\w+\s+m0,", ins[i - 2])
+               for i, l in enumerate(ins) if "global_load_lds" in l), ins
