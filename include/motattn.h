@@ -100,7 +100,8 @@ const char* mot_status_string(mot_status s);
  * frame -> view -> row -> col.
  * Errors: INVALID_ARG for null pointers, bad enums, empty segments, a
  * segment order that breaks §2 (AR, then clean, then noisy; vision, audio,
- * action inside a DM group) or N > capacity.  When the segments are valid,
+ * action inside a DM group), token counts or frame / step indices past
+ * int64, or N > capacity.  When the segments are valid,
  * *n_tok_out and *n_ar_out receive N and n_ar even if N > capacity, so a
  * first call with capacity 0 (buffers may then be NULL) sizes the buffers;
  * otherwise they receive 0. */

@@ -27,9 +27,14 @@ int dm_class(int32_t kind) {
   }
 }
 
+// Tokens of a segment, or -1 when the count does not fit in int64.
 int64_t seg_count(const mot_segment& s) {
-  if (s.kind == MOT_KIND_VIDEO) return s.n_frames * s.n_views * s.grid_h * s.grid_w;
-  return s.n_tokens;
+  if (s.kind != MOT_KIND_VIDEO) return s.n_tokens;
+  int64_t c = s.n_frames;
+  if (__builtin_mul_overflow(c, s.n_views, &c) || __builtin_mul_overflow(c, s.grid_h, &c) ||
+      __builtin_mul_overflow(c, s.grid_w, &c))
+    return -1;
+  return c;
 }
 
 bool seg_valid(const mot_segment& s) {
@@ -38,11 +43,12 @@ bool seg_valid(const mot_segment& s) {
   if (s.kind == MOT_KIND_VIDEO) {
     if (s.n_frames <= 0 || s.n_views <= 0 || s.grid_h <= 0 || s.grid_w <= 0) return false;
     if (!(s.rate > 0.0)) return false;
+    if (s.frame0 > INT64_MAX - s.n_frames) return false;  // frame indices stay in int64
   } else {
     if (s.n_tokens <= 0) return false;
     if ((s.kind == MOT_KIND_AUDIO || s.kind == MOT_KIND_ACTION) && !(s.rate > 0.0)) return false;
     if (s.kind == MOT_KIND_AUDIO || s.kind == MOT_KIND_ACTION) {
-      if (s.step0 < 0) return false;
+      if (s.step0 < 0 || s.step0 > INT64_MAX - s.n_tokens) return false;
     }
   }
   if (s.region == MOT_REGION_AR) return s.kind == MOT_KIND_TEXT || s.kind == MOT_KIND_SPECIAL;
@@ -74,7 +80,8 @@ extern "C" mot_status mot_build_layout(const mot_segment* segs, int32_t n_segs,
   for (int32_t a = 0; a < n_segs; ++a) {
     const mot_segment& s = segs[a];
     if (!seg_valid(s)) return MOT_ERR_INVALID_ARG;
-    int64_t c = seg_count(s);
+    const int64_t c = seg_count(s);
+    if (c < 0 || c > INT64_MAX - n) return MOT_ERR_INVALID_ARG;  // count past int64
     if (s.region == MOT_REGION_AR) {
       if (seen_dm) return MOT_ERR_INVALID_ARG;
       n_ar += c;

@@ -84,6 +84,27 @@ def test_layout_rejects_bad_order(segs):
         mot.mot_build_layout(segs)
 
 
+def test_layout_rejects_counts_past_int64():
+    def status(segs):
+        arr = (mot.mot_segment * len(segs))(*segs)
+        n, n_ar = ctypes.c_int64(0), ctypes.c_int64(0)
+        return mot.raw_call("mot_build_layout", arr, len(segs), 0, ctypes.byref(n),
+                            ctypes.byref(n_ar), None, None), n.value
+
+    text = mot.mot_segment(W.AR, W.TEXT, 4, 0, 1, 0, 0, 0.0, -1, 0)
+    big_video = mot.mot_segment(W.DM_NOISY, W.VIDEO, 0, 1 << 40, 1 << 20, 1 << 10, 1 << 10, 24.0, -1, 0)
+    assert status([text, big_video]) == (mot.MOT_ERR_INVALID_ARG, 0)
+    half = mot.mot_segment(W.AR, W.TEXT, 1 << 62, 0, 1, 0, 0, 0.0, -1, 0)
+    assert status([half, half, half, half]) == (mot.MOT_ERR_INVALID_ARG, 0)
+    late = mot.mot_segment(W.DM_NOISY, W.VIDEO, 0, 2, 1, 4, 4, 24.0, (1 << 63) - 1, 0)
+    assert status([text, late]) == (mot.MOT_ERR_INVALID_ARG, 0)
+    far = mot.mot_segment(W.DM_NOISY, W.ACTION, 8, 0, 1, 0, 0, 15.0, -1, (1 << 63) - 4)
+    assert status([text, far]) == (mot.MOT_ERR_INVALID_ARG, 0)
+    # the largest counts that fit are sized, not rejected
+    ok = mot.mot_segment(W.DM_NOISY, W.VIDEO, 0, 1 << 20, 1 << 20, 1 << 10, 1 << 10, 24.0, -1, 0)
+    assert status([text, ok]) == (mot.MOT_ERR_INVALID_ARG, 4 + (1 << 60))
+
+
 @pytest.mark.parametrize("case", [
     dict(nq=25474, nk=25474, q0=0, mask=W.AR_CAUSAL_DM_FULL, n_ar=514),
     dict(nq=2451, nk=2451, q0=0, mask=W.AR_CAUSAL_DM_FULL, n_ar=258),
