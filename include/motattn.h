@@ -214,7 +214,9 @@ mot_status mot_sigma_schedule(int32_t n_steps, double shift, float* sigmas_host)
 mot_status mot_mask_materialize(const mot_attn_args* args, uint8_t* mask_dev, int32_t bm,
                                 int32_t bn, uint8_t* tiles_dev, void* stream);
 
-/* Host version of the tile classifier, into a HOST buffer. */
+/* Host version of the tile classifier, into a HOST buffer of
+ * ceil(nq/bm) * ceil(nk/bn) bytes.  INVALID_ARG for null pointers, bm or
+ * bn < 1, or mask fields that mot_attention_fwd would reject. */
 mot_status mot_tile_classes_host(const mot_attn_args* args, int32_t bm, int32_t bn,
                                  uint8_t* tiles_host);
 
