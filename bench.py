@@ -186,10 +186,20 @@ def cpu_baseline(wl, budget_s=15.0):
                 flops += oattn.flops((r1 - r0) * n, 1, d)
                 rows_done += r1 - r0
                 r0 = r1
+    # and one block of 256 DM rows of a fresh head on a single thread
+    q, k, v = (rng.standard_normal((n, 1, d)).astype(np.float32) for _ in range(3))
+    with threadpool_limits(limits=1):
+        r1 = min(n, n_ar + 256)
+        t1 = time.perf_counter()
+        oattn.attention(q[n_ar:r1], k, v, n_ar, W.AR_CAUSAL_DM_FULL, n_ar=n_ar)
+        dt1 = time.perf_counter() - t1
+        one_core = oattn.flops((r1 - n_ar) * n, 1, d) / max(dt1, 1e-9) / 1e12
     return {"value": flops / max(dt, 1e-9) / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "single_core_value": one_core,
             "sample": "fp64 oracle attention over %d DM query rows x %d keys (%d of %d heads "
-                      "started, one head at a time), %.1f s of oracle time on %s, %d BLAS threads"
-                      % (rows_done, n, heads, wl.n_heads, dt, _cpu_model(), cores)}
+                      "started, one head at a time), %.1f s of oracle time on %s, %d BLAS threads; "
+                      "single_core_value: one block of %d DM rows on 1 thread, %.2f s"
+                      % (rows_done, n, heads, wl.n_heads, dt, _cpu_model(), cores, r1 - n_ar, dt1)}
 
 
 def main():

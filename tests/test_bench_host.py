@@ -105,7 +105,7 @@ def test_cpu_baseline_reports_a_bounded_oracle_sample():
     wl = W.BY_NAME["tiny_fp32"]
     cb = bench.cpu_baseline(wl, budget_s=0.5)
     assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["cores"] >= 1
-    assert cb["value"] > 0
+    assert cb["value"] > 0 and cb["single_core_value"] > 0
     n_ar = W.region_counts(wl.segments)[0]
     # every DM row of every head, as the tiny workload fits the budget
     assert "%d DM query rows" % ((wl.n_tokens - n_ar) * wl.n_heads) in cb["sample"]
