@@ -83,10 +83,11 @@ struct AttnParams {
 constexpr int BN = 64;                  // keys per tile
 constexpr int NST = BN / 32;            // 32-key MFMA blocks per tile
 constexpr float OVERFLOW_SUM = 18446744073709551616.f;  // 2^64: a lane's tile sum above this moves the reference
-#ifndef MOT_ATTN_WAVES
-#define MOT_ATTN_WAVES 4
-#endif
-constexpr int ATTN_WAVES = MOT_ATTN_WAVES;  // waves per workgroup (32 query rows each)
+// Waves per workgroup (32 query rows each).  Fixed at 4: the only shape
+// whose LDS ring, copy count and occupancy have run on the GPU.  An 8-wave
+// shape with a 128 KB ring faulted once with no cause found, so no build
+// switch selects another count.
+constexpr int ATTN_WAVES = 4;
 
 template <int D>
 struct Lay {
@@ -452,6 +453,7 @@ template <int D, int W, bool ROPE_Q>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma(AttnParams p) {
   using L = Lay<D>;
+  static_assert(W == 4, "only the 4-wave workgroup shape is built");
   static_assert(L::BYTES <= 65536, "LDS copies stay below 64 KB");
   constexpr int BM = 32 * W;
   constexpr int KSTEPS = D / 16;

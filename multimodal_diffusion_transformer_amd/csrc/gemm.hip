@@ -414,8 +414,12 @@ __global__ __launch_bounds__(256) void gemm_region_f32(const float* x, const flo
   const int tx = threadIdx.x % FT, ty = threadIdx.x / FT;
   const int64_t row = (int64_t)blockIdx.y * FT + ty;
   const int64_t col = (int64_t)blockIdx.x * FT + tx;
+  // the tile's rows clipped to [0, M): a room's weights are read only when
+  // one of the tile's real rows belongs to it (the caller may pass NULL for
+  // a room with no rows)
   const int64_t rlo = (int64_t)blockIdx.y * FT;
-  const bool need_ar = rlo < n_ar, need_dm = rlo + FT > n_ar;
+  const int64_t rhi = rlo + FT < M ? rlo + FT : M;  // exclusive
+  const bool need_ar = rlo < n_ar, need_dm = rhi > n_ar;
   float acc = 0.f;
   for (int64_t k0 = 0; k0 < K; k0 += FT) {
     xs[ty][tx] = (row < M && k0 + tx < K) ? x[row * K + k0 + tx] : 0.f;

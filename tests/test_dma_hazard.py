@@ -58,9 +58,54 @@ def _waits(prev):
     return int(n.group(1), 0) + 1 if n else 1
 
 
+# VOP3b forms whose second operand is a scalar destination (carry / scale)
+_VOP3B_SDST = re.compile(r"v_(add|sub|subrev|addc|subb|subbrev)_co_|v_div_scale_|v_mad_(u64_u32|i64_i32)")
+
+
+def _sregs(tok):
+    """Scalar register numbers named by one operand token (sN or s[a:b])."""
+    m = re.fullmatch(r"s(\d+)", tok)
+    if m:
+        return {int(m.group(1))}
+    m = re.fullmatch(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    return set()
+
+
+def _vector_sgpr_writes(line):
+    """Scalar registers a vector instruction writes: the first operand of
+    v_readfirstlane / v_readlane / an e64 compare, the second of a VOP3b form
+    (carry-out or scale)."""
+    m = re.match(r"(v_\w+)\s+(.*)", line)
+    if not m:
+        return set()
+    ops = [o.strip() for o in m.group(2).split("//")[0].split(",")]
+    out = set()
+    if ops:
+        out |= _sregs(ops[0])
+    if len(ops) > 1 and _VOP3B_SDST.match(m.group(1)):
+        out |= _sregs(ops[1])
+    return out
+
+
+_SALU_NO_DEST = re.compile(r"s_(cmp|bitcmp|cbranch|branch|waitcnt|nop|setprio|barrier|sleep|endpgm|"
+                          r"sendmsg|store|buffer_store|dcache|trap|set|ttrace|icache)")
+
+
+def _scalar_writes(line):
+    """Scalar registers a scalar instruction writes (its first operand)."""
+    m = re.match(r"(s_\w+)\s+(.*)", line)
+    if not m or _SALU_NO_DEST.match(m.group(1)):
+        return set()
+    return _sregs(m.group(2).split("//")[0].split(",")[0].strip())
+
+
 def _hazards(kernels):
-    """(copies, list of copies whose base a v_readfirstlane wrote with fewer
-    than WAIT_STATES wait states in between)."""
+    """(copies, list of copies whose base a vector instruction wrote with
+    fewer than WAIT_STATES wait states in between).  Walking back from the
+    copy, a register that a scalar instruction wrote later than any vector
+    write is defined by that scalar write and drops out of the search."""
     copies = 0
     report = []
     for name, ins in kernels.items():
@@ -69,16 +114,44 @@ def _hazards(kernels):
             if not m:
                 continue
             copies += 1
-            regs = {m.group(1), m.group(2)}
+            live = set(range(int(m.group(1)), int(m.group(2)) + 1))
             waits = 0  # wait states between the candidate writer and the copy
             for prev in reversed(ins[max(0, i - WINDOW):i]):
-                w = re.search(r"v_readfirstlane_b32\s+s(\d+),", prev)
-                if w and w.group(1) in regs:
+                if _vector_sgpr_writes(prev) & live:
                     if waits < WAIT_STATES:
                         report.append("%s: %s" % (name[:60], line))
                     break
+                live -= _scalar_writes(prev)
+                if not live:
+                    break
                 waits += _waits(prev)
     return copies, report
+
+
+def test_scan_recognises_every_vector_write_of_a_scalar_register():
+    # the forms a compiler may use to move a vector-computed value or flag
+    # into scalar registers, each followed at once by a copy from them
+    writers = ["v_readfirstlane_b32 s4, v1", "v_readlane_b32 s5, v2, 3",
+               "v_cmp_eq_u32_e64 s[4:5], v1, v2", "v_add_co_u32_e64 v1, s[4:5], v2, v3",
+               "v_addc_co_u32_e64 v1, s[4:5], v2, v3, vcc", "v_mad_u64_u32 v[2:3], s[4:5], v1, v2, 0"]
+    for w in writers:
+        ins = [w, "global_load_lds_dwordx4 v0, s[4:5]"]
+        assert _hazards({"k": ins})[1], w
+        ok = [w, "s_nop 4", "global_load_lds_dwordx4 v0, s[4:5]"]
+        assert not _hazards({"k": ok})[1], w
+    # a scalar write after the vector one redefines the register
+    redefined = ["v_readlane_b32 s4, v255, 11", "s_mov_b32 m0, s4", "s_add_u32 s4, s8, s9",
+                 "s_addc_u32 s5, s9, 0", "global_load_lds_dwordx4 v0, s[4:5]"]
+    assert not _hazards({"k": redefined})[1]
+    half = ["v_readlane_b32 s5, v255, 11", "s_add_u32 s4, s8, s9", "global_load_lds_dwordx4 v0, s[4:5]"]
+    assert _hazards({"k": half})[1]
+    # a compare writes SCC only
+    assert _hazards({"k": ["v_readfirstlane_b32 s4, v1", "s_cmp_eq_u32 s4, 0",
+                           "global_load_lds_dwordx4 v0, s[4:5]"]})[1]
+    # reading a scalar register in a vector instruction writes nothing
+    for r in ["v_add_u32_e32 v1, s4, v1", "v_cndmask_b32_e64 v1, v2, v3, s[4:5]",
+              "v_mov_b32_e32 v1, s5"]:
+        assert not _hazards({"k": [r, "global_load_lds_dwordx4 v0, s[4:5]"]})[1], r
 
 
 def _m0_hazards(kernels):
