@@ -153,10 +153,11 @@ def mot_build_layout(segments):
 
 
 def mot_qkv_project(x, w_ar, w_dm, y, n_ar, stream=None):
-    """y[r] = x[r] @ (r < n_ar ? w_ar : w_dm); contiguous row-major tensors."""
+    """y[r] = x[r] @ (r < n_ar ? w_ar : w_dm); contiguous row-major tensors.
+    A room with no rows may pass None for its weights."""
     _need_cuda(x, w_ar, w_dm, y)
     for t in (x, w_ar, w_dm, y):
-        if not t.is_contiguous():
+        if t is not None and not t.is_contiguous():
             raise ValueError("mot_qkv_project takes contiguous tensors")
     n_rows, d_in = x.shape
     d_out = y.shape[1]

@@ -89,6 +89,54 @@ def test_attention_fp32_tiny_workload_full():
     assert_parity(to_np(O), want, "fp32", "tiny fp32")
 
 
+F32_CASES = [
+    # name, nq, nk, q0, mode, n_ar, n_prefix, chunk_len, d
+    ("f32_ar_d128", 150, 150, 0, AR, 40, 0, 0, 128),
+    ("f32_ar_qoffset_d128", 70, 230, 160, AR, 100, 0, 0, 128),
+    ("f32_chunk_d64", 3 * 37 + 5, 20 + 3 * 37 + 5, 20, CH, 0, 20, 37, 64),
+    ("f32_chunk_d128", 2 * 45 + 7, 33 + 2 * 45 + 7, 33, CH, 0, 33, 45, 128),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_attention_fp32_parity(case):
+    """The fp32 kernel at both head sizes and in both mask modes, with the
+    LSE, against the oracle at the fp32 tolerance."""
+    name, nq, nk, q0, mode, n_ar, n_prefix, chunk_len, d = case
+    dev = device()
+    mot = _mot()
+    h = 3
+    say("attention %s nq=%d nk=%d q0=%d d=%d" % (name, nq, nk, q0, d))
+    q, k, v = _qkv(12, nq, nk, h, d, "fp32")
+    Q, K, V = _to_dev(q, k, v, dev, packed=True)
+    O = torch.empty((nq, h, d), dtype=torch.float32, device=dev)
+    L = torch.empty((h, nq), dtype=torch.float32, device=dev)
+    mot.mot_attention_fwd(Q, K, V, O, mask=mode, q0=q0, n_ar=n_ar, n_prefix=n_prefix,
+                          chunk_len=chunk_len, lse=L)
+    torch.cuda.synchronize()
+    want, lse = oattn.attention(q.f32, k.f32, v.f32, q0, mode, n_ar, n_prefix, max(chunk_len, 1))
+    assert_parity(to_np(O), want, "fp32", name)
+    np.testing.assert_allclose(to_np(L), lse, atol=1e-4, rtol=0)
+
+
+def test_attention_run_twice_is_bitwise_deterministic():
+    """The same launch twice gives the same bits (no atomics, no order
+    that depends on scheduling), for both kernels."""
+    dev = device()
+    mot = _mot()
+    for dtype, n, d in (("bf16", 1100, 128), ("fp32", 200, 64)):
+        q, k, v = _qkv(13, n, n, 4, d, dtype)
+        Q, K, V = _to_dev(q, k, v, dev, packed=True)
+        outs = []
+        for _ in range(2):
+            O = torch.empty((n, 4, d), dtype=Q.dtype, device=dev)
+            L = torch.empty((4, n), dtype=torch.float32, device=dev)
+            mot.mot_attention_fwd(Q, K, V, O, mask=AR, n_ar=300, lse=L)
+            outs.append((O, L))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), dtype
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
 @pytest.mark.parametrize("rope_k", [False, True])
 def test_attention_fused_rope_on_load(dtype, d, rope_k):

@@ -67,6 +67,26 @@ def test_projection_fp32_tiny_workload():
     assert_parity(to_np(Y), want, "fp32", "tiny fp32 qkv")
 
 
+@pytest.mark.parametrize("n_rows,n_ar", [(20, 20), (20, 0), (37, 37), (1, 1)])
+def test_projection_fp32_room_without_rows_needs_no_weights(n_rows, n_ar):
+    """A room with no rows may pass NULL weights: the fp32 kernel's last
+    16-row tile runs past the rows, and must not read the missing room's
+    weights for those phantom rows."""
+    dev = device()
+    mot = _mot()
+    say("projection fp32 n_rows=%d n_ar=%d, the empty room's weights NULL" % (n_rows, n_ar))
+    x = W.make(23, 0, (n_rows, 48), "fp32")
+    w = W.make(23, 1, (48, 40), "fp32", 0.02)
+    Y = torch.empty((n_rows, 40), dtype=torch.float32, device=dev)
+    Wt = W.to_torch(w, dev)
+    if n_ar == n_rows:
+        mot.mot_qkv_project(W.to_torch(x, dev), Wt, None, Y, n_ar)
+    else:
+        mot.mot_qkv_project(W.to_torch(x, dev), None, Wt, Y, n_ar)
+    torch.cuda.synchronize()
+    assert_parity(to_np(Y), oproj.project_rows(x.f32, w.f32), "fp32", "fp32 one room")
+
+
 def test_projection_ar_rows_ignore_generator_weights():
     dev = device()
     mot = _mot()
