@@ -28,6 +28,8 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Device calls only enqueue work on it; they never synchronize.
  *   - bf16 is bfloat16 (1-8-7), stored as 16-bit words; fp32 is IEEE float.
+ *   - Element types are passed as int32_t holding a mot_dtype; any other
+ *     value is MOT_ERR_INVALID_ARG.
  *   - Strides are in elements.  Device pointers must be 16-byte aligned and
  *     strides multiples of 8 elements (bf16) / 4 elements (fp32) unless a
  *     call says otherwise.
@@ -87,7 +89,9 @@ typedef struct {
 } mot_segment;
 
 int mot_abi_version(void);
-const char* mot_status_string(mot_status s);
+/* Text of a status code; any other value gives "unknown status".  Takes
+ * the code as an int32_t, so a C caller may pass any value. */
+const char* mot_status_string(int32_t s);
 
 /* Packed-sequence layout (method page §2 and §5), host only.
  * Writes per-token region tags (uint8, mot_region) and (t, h, w) positions
@@ -125,7 +129,7 @@ mot_status mot_build_layout(const mot_segment* segs, int32_t n_segs, int64_t cap
  * d_out <= 2^28 - 16. */
 mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, void* y,
                            int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
-                           mot_dtype in_dt, mot_dtype out_dt, void* stream);
+                           int32_t in_dt, int32_t out_dt, void* stream);
 
 /* Unified 3D mRoPE (method page §5), in place on x [n_tok][n_heads][head_dim]
  * with element strides tok_stride / head_stride (the last dim contiguous).
@@ -135,7 +139,7 @@ mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, vo
  * are evaluated in fp64, the rotation in fp32, the store rounds RNE.
  * head_dim in {64, 128}; sec_t+sec_h+sec_w == head_dim/2; all >= 0.
  * n_tok == 0 is a no-op.  Dispatch limit: n_tok * head_dim/8 <= 2^32 - 256. */
-mot_status mrope_apply(void* x, mot_dtype dt, int64_t n_tok, int32_t n_heads, int32_t head_dim,
+mot_status mrope_apply(void* x, int32_t dt, int64_t n_tok, int32_t n_heads, int32_t head_dim,
                        int64_t tok_stride, int64_t head_stride, const float* pos_thw,
                        int32_t sec_t, int32_t sec_h, int32_t sec_w, float theta, void* stream);
 
@@ -190,7 +194,7 @@ mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
  * (sigma_next - sigma) is formed in fp32 and applied with one fused
  * multiply-add.  x_bf16 (nullable): also store bf16(x_new) there (the row
  * block of the next step's packed input).  n == 0 is a no-op. */
-mot_status flow_euler_step(float* x, const void* v, mot_dtype v_dt, int64_t n,
+mot_status flow_euler_step(float* x, const void* v, int32_t v_dt, int64_t n,
                            float sigma, float sigma_next, void* x_bf16, void* stream);
 
 /* Sampler noise levels with the flow shift (method page §6.3 shift map, §7.2
@@ -202,7 +206,8 @@ mot_status flow_euler_step(float* x, const void* v, mot_dtype v_dt, int64_t n,
  * sigma_0 = 1 and sigma_n = 0; shift = 1 gives sigma_k = 1 - k/n_steps.
  * Consecutive pairs (sigma_k, sigma_k+1) are the arguments of
  * flow_euler_step.  Errors: INVALID_ARG for n_steps < 1, a null buffer, or a
- * shift that is not positive and finite. */
+ * shift outside [2^-20, 2^20] (the pages use 1 to 10; far below that range
+ * the denominator cancels). */
 mot_status mot_sigma_schedule(int32_t n_steps, double shift, float* sigmas_host);
 
 /* Debug/test helpers: the exact mask and the tile classes the attention

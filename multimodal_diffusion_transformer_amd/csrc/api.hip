@@ -68,7 +68,7 @@ using namespace mot;
 
 extern "C" int mot_abi_version(void) { return MOT_ABI_VERSION; }
 
-extern "C" const char* mot_status_string(mot_status s) {
+extern "C" const char* mot_status_string(int32_t s) {
   switch (s) {
     case MOT_OK: return "ok";
     case MOT_ERR_INVALID_ARG: return "invalid argument";
@@ -124,7 +124,7 @@ extern "C" mot_status mot_attention_fwd(const mot_attn_args* a, void* stream) {
 
 extern "C" mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, void* y,
                                       int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
-                                      mot_dtype in_dt, mot_dtype out_dt, void* stream) {
+                                      int32_t in_dt, int32_t out_dt, void* stream) {
   if (n_rows < 0 || n_ar < 0 || n_ar > n_rows || d_in <= 0 || d_out <= 0) return MOT_ERR_INVALID_ARG;
   if (n_rows == 0) return MOT_OK;
   if (!x || !y || (n_ar > 0 && !w_ar) || (n_ar < n_rows && !w_dm)) return MOT_ERR_INVALID_ARG;
@@ -133,9 +133,9 @@ extern "C" mot_status mot_qkv_project(const void* x, const void* w_ar, const voi
   if (((uintptr_t)x | (uintptr_t)w_ar | (uintptr_t)w_dm | (uintptr_t)y) & 15) return MOT_ERR_INVALID_ARG;
   if (in_dt == MOT_BF16 && (d_in % 64 || d_out % 64)) return MOT_ERR_UNSUPPORTED;
   if (in_dt == MOT_FP32 && out_dt != MOT_FP32) return MOT_ERR_UNSUPPORTED;
-  if (!region_gemm_fits(n_rows, n_ar, d_out, in_dt)) return MOT_ERR_UNSUPPORTED;
-  hipError_t e = region_gemm(x, w_ar, w_dm, y, n_rows, n_ar, d_in, d_out, in_dt, out_dt,
-                             (hipStream_t)stream);
+  if (!region_gemm_fits(n_rows, n_ar, d_out, (mot_dtype)in_dt)) return MOT_ERR_UNSUPPORTED;
+  hipError_t e = region_gemm(x, w_ar, w_dm, y, n_rows, n_ar, d_in, d_out, (mot_dtype)in_dt,
+                             (mot_dtype)out_dt, (hipStream_t)stream);
   return e == hipSuccess ? MOT_OK : MOT_ERR_HIP;
 }
 

@@ -53,6 +53,7 @@
 //    that XCD's L2; query tiles are issued heaviest first.
 #include <atomic>
 
+#include "attn_tiles.hpp"
 #include "common.hpp"
 #include "rope_dev.hpp"
 
@@ -80,37 +81,12 @@ struct AttnParams {
   RopeTable rope;
 };
 
-constexpr int BN = 64;                  // keys per tile
-constexpr int NST = BN / 32;            // 32-key MFMA blocks per tile
 constexpr float OVERFLOW_SUM = 18446744073709551616.f;  // 2^64: a lane's tile sum above this moves the reference
 // Waves per workgroup (32 query rows each).  Fixed at 4: the only shape
 // whose LDS ring, copy count and occupancy have run on the GPU.  An 8-wave
 // shape with a 128 KB ring faulted once with no cause found, so no build
 // switch selects another count.
 constexpr int ATTN_WAVES = 4;
-
-template <int D>
-struct Lay {
-  static constexpr int CH = D / 8;          // 16-byte chunks per row
-  static constexpr int ROWB = D * 2;        // bytes per row
-  static constexpr int TILE_B = BN * ROWB;  // one K or V tile
-  static constexpr int BYTES = 4 * TILE_B;  // K ring (2) + V ring (2)
-  static constexpr int RPG = 16 / CH;       // rows per 256-byte bank cycle
-  static constexpr int RPI = 64 / CH;       // rows per wave-wide 1 KB load
-  static constexpr int NINSTR = BN / RPI;   // 1 KB loads per tile
-};
-
-// Chunk swizzles: logical 16-byte chunk c of row r lives at chunk c ^ f(r).
-// K rows are read in key_perm order, so one 8-lane group touches rows
-// {0..3, 16..19} (+4, +8, ...): the K swizzle gives those eight rows eight
-// different chunks (D=128: bits 0-1, 4, 2 of r; D=64: rows are 128 B, so bit
-// 0 picks the bank half and bits 1, 2, 4 the chunk).  V is read four rows
-// at a time by 16-lane groups; its swizzle separates rows r%4.
-template <int D> __device__ __forceinline__ int swz_k(int r) {
-  if constexpr (D == 128) return (r & 3) | (((r >> 4) & 1) << 2) | (((r >> 2) & 1) << 3);
-  else return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 4) & 1) << 2);
-}
-template <int D> __device__ __forceinline__ int swz_v(int r) { return 4 * ((r / Lay<D>::RPG) % (Lay<D>::CH / 4)); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -154,42 +130,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 __device__ __forceinline__ void wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Row of the K tile that feeds MFMA row rho so that lane half g holds keys
-// 16g..16g+15 in accumulator registers 0..15.
-__device__ __forceinline__ int key_perm(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
-
+// Issues the LDS-DMA copies of K and V tiles; the address arithmetic is
+// TileAddr's (attn_tiles.hpp), which a host program checks for every copy.
 template <int D, int W>
 struct TileLoader {
-  static constexpr int PER_WAVE = Lay<D>::NINSTR / W;
-  static_assert(PER_WAVE >= 1 && Lay<D>::NINSTR % W == 0, "loads per wave");
-  // Load i of a wave copies tile row r = RPI (wave PER_WAVE + i) + lane / CH,
-  // and its chunk depends on r only through the swizzle.  With RPI = 64 / CH
-  // rows per load, the swizzle bits that vary with i are bit 2 of r at
-  // D = 128 (so only i & 1 matters) and none at D = 64, or for V: the lane
-  // part of the byte offset takes NVAR_K values over i for K and one for V.
-  static constexpr int NVAR_K = D == 128 ? 2 : 1;
-  uint32_t lk[NVAR_K], lv;  // lane parts of the byte offsets
+  using A = TileAddr<D, W>;
+  static constexpr int PER_WAVE = A::PER_WAVE;
+  static constexpr int NVAR_K = A::NVAR_K;
+  uint32_t lk[NVAR_K], lv;    // lane parts of the byte offsets
   uint32_t k_row_b, v_row_b;  // bytes per RPI rows (wave-uniform)
   int wave;                   // wave-uniform
 
-  __device__ __forceinline__ static int row_of(int wave, int i, int lane) {
-    return (wave * PER_WAVE + i) * Lay<D>::RPI + lane / Lay<D>::CH;
-  }
-  template <bool IS_K>
-  __device__ __forceinline__ static int chunk_of(int r, int lane) {
-    return (lane % Lay<D>::CH) ^ (IS_K ? swz_k<D>(r) : swz_v<D>(r));
-  }
-
   __device__ __forceinline__ void init(int wave_, int lane, int64_t k_ts, int64_t v_ts) {
     wave = wave_;
-    k_row_b = (uint32_t)(Lay<D>::RPI * k_ts * 2);
-    v_row_b = (uint32_t)(Lay<D>::RPI * v_ts * 2);
+    k_row_b = A::row_bytes(k_ts);
+    v_row_b = A::row_bytes(v_ts);
 #pragma unroll
-    for (int i = 0; i < NVAR_K; ++i) {
-      const int r = row_of(wave, i, lane);
-      lk[i] = (uint32_t)((lane / Lay<D>::CH) * k_ts * 2 + chunk_of<true>(r, lane) * 16);
-    }
-    lv = (uint32_t)((lane / Lay<D>::CH) * v_ts * 2 + chunk_of<false>(row_of(wave, 0, lane), lane) * 16);
+    for (int i = 0; i < NVAR_K; ++i) lk[i] = A::template lane_off<true>(wave, i, lane, k_ts);
+    lv = A::template lane_off<false>(wave, 0, lane, v_ts);
   }
 
   // Issue this wave's share of one tile (K or V) starting at key kbase into
@@ -199,23 +157,21 @@ struct TileLoader {
   __device__ __forceinline__ void issue(const AttnParams& p, int head, int64_t kbase, unsigned char* dst) const {
     const int64_t ts = IS_K ? p.k_ts : p.v_ts;
     const char* base = reinterpret_cast<const char*>(IS_K ? p.k : p.v) +
-                       (kbase * ts + (int64_t)head * (IS_K ? p.k_hs : p.v_hs)) * 2;
+                       A::tile_base_el(kbase, ts, head, IS_K ? p.k_hs : p.v_hs) * 2;
     const int64_t last = p.m.nk - 1 - kbase;  // last valid tile row
     if (__builtin_expect(last >= BN - 1, 1)) {
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int n = wave * PER_WAVE + i;
-        const uint32_t rows_b = (uint32_t)n * (IS_K ? k_row_b : v_row_b);  // wave-uniform
-        dma16(base + rows_b, IS_K ? lk[i % NVAR_K] : lv, lds_addr(dst + n * 1024));
+        const uint32_t rows_b = A::rows_bytes(n, IS_K ? k_row_b : v_row_b);  // wave-uniform
+        dma16(base + rows_b, IS_K ? lk[i % NVAR_K] : lv, lds_addr(dst + A::lds_dst(n, 0)));
       }
     } else {  // the ragged last tile: full per-lane offsets from the tile base
       const int lane = threadIdx.x & 63;
 #pragma unroll
       for (int i = 0; i < PER_WAVE; ++i) {
         const int n = wave * PER_WAVE + i;
-        const int r = row_of(wave, i, lane);
-        const int64_t rr = r > last ? last : r;  // never negative: the lane offset is unsigned
-        dma16(base, (uint32_t)(rr * ts * 2 + chunk_of<IS_K>(r, lane) * 16), lds_addr(dst + n * 1024));
+        dma16(base, A::template ragged_off<IS_K>(wave, i, lane, ts, last), lds_addr(dst + A::lds_dst(n, 0)));
       }
     }
   }
@@ -516,22 +472,10 @@ void attn_fwd_mfma(AttnParams p) {
   }
 
   // ---- loop-invariant LDS read offsets ----
-  {
-    const int row = key_perm(l32);
-    const int f = swz_k<D>(row);
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) ws.kaddr[s] = row * L::ROWB + (((2 * s + g) ^ f) * 16);
-  }
-  {
-    const int j = lane & 15, q16 = (lane >> 4) & 1;
-    const int rowl = 16 * g + j / 4;  // + 32st + 8t + 4h, all multiples of 4
-    const int f = swz_v<D>(rowl);     // so the swizzle is the same for all of them
+  for (int s = 0; s < KSTEPS; ++s) ws.kaddr[s] = k_read_off<D>(s, lane);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int c = 4 * dt + 2 * q16 + (j & 3) / 2;
-      ws.vaddr[dt] = rowl * L::ROWB + ((c ^ f) * 16) + 8 * (j & 1);
-    }
-  }
+  for (int dt = 0; dt < DT; ++dt) ws.vaddr[dt] = v_read_off<D>(dt, lane);
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll

@@ -78,7 +78,7 @@ static void launch(float* x, const void* v, int64_t n, float dt, bf16_t* xb, hip
 
 }  // namespace mot
 
-extern "C" mot_status flow_euler_step(float* x, const void* v, mot_dtype v_dt, int64_t n,
+extern "C" mot_status flow_euler_step(float* x, const void* v, int32_t v_dt, int64_t n,
                                       float sigma, float sigma_next, void* x_bf16,
                                       void* stream) {
   using namespace mot;

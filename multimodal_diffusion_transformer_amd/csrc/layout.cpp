@@ -74,6 +74,7 @@ extern "C" mot_status mot_build_layout(const mot_segment* segs, int32_t n_segs,
   *n_ar_out = 0;
   // Validate and count; enforce the §2 order.
   int64_t n = 0, n_ar = 0;
+  int64_t frames = 0;  // running latent-frame count (a video segment with frame0 < 0 continues it)
   bool seen_dm = false;
   int32_t last_region = MOT_REGION_AR;
   int last_class = -1;
@@ -82,6 +83,11 @@ extern "C" mot_status mot_build_layout(const mot_segment* segs, int32_t n_segs,
     if (!seg_valid(s)) return MOT_ERR_INVALID_ARG;
     const int64_t c = seg_count(s);
     if (c < 0 || c > INT64_MAX - n) return MOT_ERR_INVALID_ARG;  // count past int64
+    if (s.kind == MOT_KIND_VIDEO) {
+      const int64_t f0 = s.frame0 >= 0 ? s.frame0 : frames;
+      if (f0 > INT64_MAX - s.n_frames) return MOT_ERR_INVALID_ARG;  // frame index past int64
+      frames = f0 + s.n_frames;
+    }
     if (s.region == MOT_REGION_AR) {
       if (seen_dm) return MOT_ERR_INVALID_ARG;
       n_ar += c;

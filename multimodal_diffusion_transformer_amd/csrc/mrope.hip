@@ -89,7 +89,7 @@ static void launch_rope(void* x, int64_t n_tok, int n_heads, int64_t ts, int64_t
 
 }  // namespace mot
 
-extern "C" mot_status mrope_apply(void* x, mot_dtype dt, int64_t n_tok, int32_t n_heads,
+extern "C" mot_status mrope_apply(void* x, int32_t dt, int64_t n_tok, int32_t n_heads,
                                   int32_t head_dim, int64_t tok_stride, int64_t head_stride,
                                   const float* pos_thw, int32_t sec_t, int32_t sec_h,
                                   int32_t sec_w, float theta, void* stream) {

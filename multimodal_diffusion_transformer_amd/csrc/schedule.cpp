@@ -14,7 +14,9 @@
 
 extern "C" mot_status mot_sigma_schedule(int32_t n_steps, double shift, float* sigmas_host) {
   if (n_steps < 1 || !sigmas_host) return MOT_ERR_INVALID_ARG;
-  if (!(shift > 0.0) || !isfinite(shift)) return MOT_ERR_INVALID_ARG;
+  // A shift in [2^-20, 2^20]: the pages use 1 to 10.  Below the range the
+  // denominator 1 + (s - 1) loses s to cancellation (sigma_0 would not be 1).
+  if (!(shift >= 0x1p-20 && shift <= 0x1p20)) return MOT_ERR_INVALID_ARG;
   const double n = (double)n_steps;
   for (int32_t k = 0; k <= n_steps; ++k) {
     const double t_bar = (double)(n_steps - k) / n;

@@ -171,7 +171,8 @@ def test_sigma_schedule_rejects_bad_args():
     buf = np.zeros(8, dtype=np.float32)
     p = buf.ctypes.data_as(ctypes.c_void_p)
     for n, shift, ptr in [(0, 5.0, p), (-3, 5.0, p), (4, 0.0, p), (4, -2.0, p),
-                          (4, float("inf"), p), (4, float("nan"), p), (4, 5.0, None)]:
+                          (4, float("inf"), p), (4, float("nan"), p), (4, 5.0, None),
+                          (4, 2.0 ** -21, p), (4, 1e-300, p), (4, 2.0 ** 21, p)]:
         assert mot.raw_call("mot_sigma_schedule", n, ctypes.c_double(shift), ptr) == \
             mot.MOT_ERR_INVALID_ARG
     assert not buf.any()
