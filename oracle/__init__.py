@@ -18,8 +18,10 @@ Sources (the pages, by title and section):
   §5 the 3D mRoPE coordinates, Δt = 6/TPS and the AR→DM time gap of 15000;
   §6.3 the rectified-flow path x_σ = σε + (1-σ)x0, v* = ε - x0, and the
   flow shift of the noise level;
-  §7.2 the Euler update x_next = x + (σ_next - σ)·v;
-  §12.1 the recommended steps, guidance and shift per model and mode.
+  §7.2 the Euler update x_next = x + (σ_next - σ)·v and the CFG combination
+  v = v_base + w (v_cond - v_base); §7.3 the generation loop;
+  §12.1 the recommended steps, guidance and shift per model and mode;
+  §12.4 the model table (grouped Q / KV heads).
 * "NVIDIA 发布 Cosmos 3 系列四个开放权重世界模型" (news page on four new
   checkpoints), section "流式生成如何工作" (how streaming generation works):
   temporal-causal chunk attention against a key/value cache.
@@ -31,4 +33,4 @@ is "parity unpinned" except the end-to-end free-running chain of
 ``oracle.denoiser`` (see its docstring).
 """
 from . import (layout, mask, mrope, attention, projection, euler, denoiser, streaming,  # noqa: F401
-               schedule)
+               schedule, cfg)

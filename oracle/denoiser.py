@@ -45,14 +45,15 @@ def round_bf16(x) -> np.ndarray:
 
 
 def layer(X, w_qkv_ar, w_qkv_dm, w_o_ar, w_o_dm, pos, n_ar, n_heads, head_dim,
-          sections, theta, store=None):
-    """Returns dict of float64 intermediates: y, q, k, v, o, lse, z."""
+          sections, theta, store=None, n_kv_heads=None):
+    """Returns dict of float64 intermediates: y, q, k, v, o, lse, z.  With
+    n_kv_heads, K and V have that many heads (grouped, oracle.attention)."""
     if store not in (None, "bf16"):
         raise ValueError("store is None or 'bf16'")
     keep = round_bf16 if store == "bf16" else (lambda t: t)
     n = X.shape[0]
     y = keep(projection.project(X, w_qkv_ar, w_qkv_dm, n_ar))
-    q, k, v = projection.split_qkv(y, n_heads, head_dim)
+    q, k, v = projection.split_qkv(y, n_heads, head_dim, n_kv_heads)
     qr = keep(mrope.apply(q, pos, sections, theta))
     kr = keep(mrope.apply(k, pos, sections, theta))
     o, lse = attention.attention(qr, kr, v, 0, AR_CAUSAL_DM_FULL, n_ar=n_ar)

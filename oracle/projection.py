@@ -32,11 +32,17 @@ def project_rows(x_rows, w, ) -> np.ndarray:
     return np.asarray(x_rows, dtype=np.float64) @ np.asarray(w, dtype=np.float64)
 
 
-def split_qkv(y: np.ndarray, n_heads: int, head_dim: int):
-    """[N, 3*H*D] -> three [N, H, D] views (columns [Q | K | V])."""
+def split_qkv(y: np.ndarray, n_heads: int, head_dim: int, n_kv_heads=None):
+    """[N, (H + 2 H_kv) D] -> Q [N, H, D], K and V [N, H_kv, D] (columns
+    [Q | K | V], each [heads][D]); H_kv defaults to H."""
     n = y.shape[0]
-    y = y.reshape(n, 3, n_heads, head_dim)
-    return y[:, 0], y[:, 1], y[:, 2]
+    hk = n_heads if n_kv_heads is None else n_kv_heads
+    if y.shape[1] != (n_heads + 2 * hk) * head_dim:
+        raise ValueError("QKV width is not (H + 2 H_kv) D")
+    q = y[:, :n_heads * head_dim].reshape(n, n_heads, head_dim)
+    k = y[:, n_heads * head_dim:(n_heads + hk) * head_dim].reshape(n, hk, head_dim)
+    v = y[:, (n_heads + hk) * head_dim:].reshape(n, hk, head_dim)
+    return q, k, v
 
 
 def flops(n_rows: int, d_in: int, d_out: int) -> float:
