@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOT_ABI_VERSION 1
+#define MOT_ABI_VERSION 2
 
 typedef enum {
   MOT_OK = 0,
@@ -148,12 +148,24 @@ mot_status mrope_apply(void* x, int32_t dt, int64_t n_tok, int32_t n_heads, int3
  *   MOT_AR_CAUSAL_DM_FULL (method page §3):  i >= n_ar  or  j <= i
  *   MOT_CHUNK_CAUSAL_KV (streaming page):   j < n_prefix  or
  *        floor((j-n_prefix)/chunk_len) <= floor((i-n_prefix)/chunk_len)
- * q: [nq][H][D], k, v: [nk][H][D], o: [nq][H][D] with the given token and
- * head strides (elements, last dim contiguous).  lse (nullable): fp32
- * [H][nq], natural-log sum-exp of the scaled scores.  q_pos / k_pos
+ * q: [nq][H][D], k, v: [nk][H_kv][D], o: [nq][H][D] with the given token
+ * and head strides (elements, last dim contiguous).  lse (nullable): fp32
+ * [n_batch][H][nq], natural-log sum-exp of the scaled scores.  q_pos / k_pos
  * (nullable, device fp32 [nq][3] / [nk][3]): when set, Q / K are rotated by
  * mRoPE (sec_*, theta) as their tiles are loaded; otherwise they are used as
- * given.  scale == 0 means 1/sqrt(D). */
+ * given.  scale == 0 means 1/sqrt(D).
+ *
+ * Grouped key/value heads (method page §12.4 model table, Q / KV heads
+ * 16/8, 32/8, 64/8): n_kv_heads = H_kv divides H; query head h reads
+ * key/value head h / (H / H_kv).  0 means H_kv = H.
+ *
+ * Batch (method page §7.2-§7.3: the condition and baseline predictions of a
+ * guided sampler step): n_batch independent problems of the same shape and
+ * mask in one launch; problem b reads q + b q_bs, k + b k_bs, v + b v_bs
+ * and writes o + b o_bs (elements; 0 shares an input, overlapping inputs
+ * are allowed, outputs must not overlap) and lse + b H nq.  n_batch 0 means
+ * 1, and the batch strides are then ignored.  Positions are shared by the
+ * problems. */
 typedef struct {
   const void* q;
   const void* k;
@@ -173,6 +185,10 @@ typedef struct {
   int32_t sec_t, sec_h, sec_w;
   float theta;
   float scale;
+  /* ABI version 2 */
+  int32_t n_kv_heads; /* 0: n_heads */
+  int32_t n_batch;    /* 0: 1 */
+  int64_t q_bs, k_bs, v_bs, o_bs;
 } mot_attn_args;
 
 /* Flash-style masked attention, O = softmax(mask(Q K^T * scale)) V per head
@@ -184,8 +200,11 @@ typedef struct {
  * MOT_ERR_UNSUPPORTED when k_pos is set (bf16 rotates Q on load only: rotate
  * K beforehand with mrope_apply, which is also the layout a key cache keeps),
  * when nk > 2^31 - 65 or nq > 2^31 - 1, or when a 64-row tile of K or V
- * spans 4 GiB or more (128 * max(k_ts, v_ts) >= 2^32).  Dispatch limit:
- * bf16 2 * n_heads * (nq + 512) <= 2^32 - 1; fp32 nq <= 2^32 - 64. */
+ * spans 4 GiB or more (128 * max(k_ts, v_ts) >= 2^32).  INVALID_ARG also
+ * for n_kv_heads < 0 or not dividing n_heads, n_batch < 0 or > 65535, and
+ * negative or misaligned batch strides.  Dispatch limit: bf16
+ * 2 * n_heads * (nq + 512) <= 2^32 - 1; fp32 nq <= 2^32 - 64 and
+ * n_heads <= 65535. */
 mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
 
 /* Flow-matching Euler update (method page §7.2), in place:

@@ -62,13 +62,16 @@ class mot_attn_args(ctypes.Structure):
                 ("chunk_len", ctypes.c_int64),
                 ("q_pos", ctypes.c_void_p), ("k_pos", ctypes.c_void_p),
                 ("sec_t", ctypes.c_int32), ("sec_h", ctypes.c_int32), ("sec_w", ctypes.c_int32),
-                ("theta", ctypes.c_float), ("scale", ctypes.c_float)]
+                ("theta", ctypes.c_float), ("scale", ctypes.c_float),
+                ("n_kv_heads", ctypes.c_int32), ("n_batch", ctypes.c_int32),
+                ("q_bs", ctypes.c_int64), ("k_bs", ctypes.c_int64), ("v_bs", ctypes.c_int64),
+                ("o_bs", ctypes.c_int64)]
 
 
 _i64, _i32, _vp, _f32 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
 _lib.mot_abi_version.restype = ctypes.c_int
 _lib.mot_status_string.restype = ctypes.c_char_p
-_lib.mot_status_string.argtypes = [ctypes.c_int]
+_lib.mot_status_string.argtypes = [ctypes.c_int32]
 _lib.mot_build_layout.restype = ctypes.c_int
 _lib.mot_build_layout.argtypes = [ctypes.POINTER(mot_segment), _i32, _i64, ctypes.POINTER(_i64),
                                   ctypes.POINTER(_i64), _vp, _vp]
@@ -180,8 +183,20 @@ def mrope_apply(x, pos, sections, theta=10000.0, stream=None):
 
 def attn_args(q, k, v, o, *, mask, q0=0, n_ar=0, n_prefix=0, chunk_len=0, lse=None,
               q_pos=None, k_pos=None, sections=(0, 0, 0), theta=10000.0, scale=0.0):
+    """q/o [N, H, D] and k/v [N, H_kv, D] views, or with a leading batch
+    dimension [B, N, H(_kv), D] whose stride is the batch stride (0 shares
+    a tensor across the batch; overlapping views are fine for inputs)."""
+    batched = q.dim() == 4
+    if {t.dim() for t in (q, k, v, o)} != {4 if batched else 3}:
+        raise ValueError("q, k, v and o must all be 3-D, or all 4-D with a batch dimension")
+    if batched:
+        nb = q.shape[0]
+        if not (k.shape[0] == v.shape[0] == o.shape[0] == nb):
+            raise ValueError("batch sizes differ")
+        bs = [t.stride(0) for t in (q, k, v, o)]
+        q, k, v, o = (t[0] for t in (q, k, v, o))
     nq, h, d = q.shape
-    nk = k.shape[0]
+    nk, hk = k.shape[0], k.shape[1]
     for t in (q, k, v, o):
         if t.stride(2) != 1:
             raise ValueError("last dim must be contiguous")
@@ -200,6 +215,10 @@ def attn_args(q, k, v, o, *, mask, q0=0, n_ar=0, n_prefix=0, chunk_len=0, lse=No
     a.k_pos = None if k_pos is None else k_pos.data_ptr()
     a.sec_t, a.sec_h, a.sec_w = (int(s) for s in sections)
     a.theta, a.scale = float(theta), float(scale)
+    a.n_kv_heads = hk
+    if batched:
+        a.n_batch = nb
+        a.q_bs, a.k_bs, a.v_bs, a.o_bs = bs
     return a
 
 

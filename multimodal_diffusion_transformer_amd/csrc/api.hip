@@ -89,6 +89,14 @@ extern "C" mot_status mot_attention_fwd(const mot_attn_args* a, void* stream) {
   const int64_t st[8] = {a->q_ts, a->q_hs, a->k_ts, a->k_hs, a->v_ts, a->v_hs, a->o_ts, a->o_hs};
   for (int i = 0; i < 8; ++i)
     if (st[i] <= 0 || st[i] % al) return MOT_ERR_INVALID_ARG;
+  // grouped key/value heads and the batch
+  if (a->n_kv_heads < 0 || (a->n_kv_heads > 0 && a->n_heads % a->n_kv_heads)) return MOT_ERR_INVALID_ARG;
+  if (a->n_batch < 0 || a->n_batch > 65535) return MOT_ERR_INVALID_ARG;
+  if (a->n_batch > 1) {
+    const int64_t bs[4] = {a->q_bs, a->k_bs, a->v_bs, a->o_bs};
+    for (int i = 0; i < 4; ++i)
+      if (bs[i] < 0 || bs[i] % al) return MOT_ERR_INVALID_ARG;
+  }
   if (((uintptr_t)a->q | (uintptr_t)a->k | (uintptr_t)a->v | (uintptr_t)a->o) & 15)
     return MOT_ERR_INVALID_ARG;
   if ((uintptr_t)a->lse & 3) return MOT_ERR_INVALID_ARG;
@@ -101,10 +109,11 @@ extern "C" mot_status mot_attention_fwd(const mot_attn_args* a, void* stream) {
   if (a->dt == MOT_BF16 && a->k_pos) return MOT_ERR_UNSUPPORTED;
   // Dispatch size.  bf16: one workgroup per (row tile, head) with 64 lanes
   // per 32 query rows, so 2 lanes per row and head, the last tile rounded up
-  // by fewer than 512 rows.  fp32: 64 query rows of 64 lanes per workgroup
-  // along x, heads along y.
+  // by fewer than 512 rows, along x; batch items along y.  fp32: 64 query
+  // rows of 64 lanes per workgroup along x, heads along y (at most 65535),
+  // batch items along z.
   if (a->dt == MOT_BF16 ? !fits_dispatch(a->nq + 512, 2 * (int64_t)a->n_heads, 0)
-                        : !fits_dispatch(a->nq, 1, 63))
+                        : (!fits_dispatch(a->nq, 1, 63) || a->n_heads > 65535))
     return MOT_ERR_UNSUPPORTED;
   RopeTable rt;
   rt.sec_t = a->sec_t;

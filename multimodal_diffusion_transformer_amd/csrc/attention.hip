@@ -75,9 +75,12 @@ struct AttnParams {
   int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs;
   MaskSpec m;
   int n_heads;
+  int kv_group;   // query heads per key/value head
+  int xcd_heads;  // heads per XCD when n_heads % 8 == 0, else 0
   int n_qtiles;
   float c_log2;  // scale * log2(e)
   const float* q_pos;
+  int64_t q_bs, k_bs, v_bs, o_bs;  // batch strides (elements); grid y is the batch item
   RopeTable rope;
 };
 
@@ -150,13 +153,15 @@ struct TileLoader {
     lv = A::template lane_off<false>(wave, 0, lane, v_ts);
   }
 
-  // Issue this wave's share of one tile (K or V) starting at key kbase into
-  // the LDS tile at `dst`.  Rows past the last key re-read the last key
-  // (never out of range; those scores are masked and the values finite).
+  // Issue this wave's share of one tile (K or V) of key/value head `head`
+  // of `tensor` (this workgroup's batch item) starting at key kbase into the
+  // LDS tile at `dst`.  Rows past the last key re-read the last key (never
+  // out of range; those scores are masked and the values finite).
   template <bool IS_K>
-  __device__ __forceinline__ void issue(const AttnParams& p, int head, int64_t kbase, unsigned char* dst) const {
+  __device__ __forceinline__ void issue(const AttnParams& p, const bf16_t* tensor, int head, int64_t kbase,
+                                        unsigned char* dst) const {
     const int64_t ts = IS_K ? p.k_ts : p.v_ts;
-    const char* base = reinterpret_cast<const char*>(IS_K ? p.k : p.v) +
+    const char* base = reinterpret_cast<const char*>(tensor) +
                        A::tile_base_el(kbase, ts, head, IS_K ? p.k_hs : p.v_hs) * 2;
     const int64_t last = p.m.nk - 1 - kbase;  // last valid tile row
     if (__builtin_expect(last >= BN - 1, 1)) {
@@ -330,13 +335,13 @@ __device__ __forceinline__ void mask_tile(f32x16_t (&sc)[NST], int lim, int kbas
 // Scores of one 32-key block of tile kbase, recomputed from K in global
 // memory, masked like the tile.
 template <int D>
-__device__ __forceinline__ f32x16_t block_scores(const AttnParams& p, const WaveState<D>& ws, int head, int kbase, int st,
-                                        bool partial, int lane) {
+__device__ __forceinline__ f32x16_t block_scores(const AttnParams& p, const WaveState<D>& ws, const bf16_t* kb,
+                                                 int kvh, int kbase, int st, bool partial, int lane) {
   constexpr int KSTEPS = WaveState<D>::KSTEPS;
   const int g = lane >> 5;
   int64_t key = (int64_t)kbase + key_perm(lane & 31) + 32 * st;
   if (key > p.m.nk - 1) key = p.m.nk - 1;  // masked below; any valid row will do
-  const bf16_t* row = p.k + key * p.k_ts + (int64_t)head * p.k_hs;
+  const bf16_t* row = kb + key * p.k_ts + (int64_t)kvh * p.k_hs;
   f32x16_t sc = {};
   // two k-steps at a time (few registers; this path is rare): the fence
   // keeps the loads from being hoisted together
@@ -364,12 +369,13 @@ __device__ __forceinline__ f32x16_t block_scores(const AttnParams& p, const Wave
 // the tile max where that is higher, O and the running sum (which already
 // hold P(j-1)) are rescaled, and P(j) and its sum are redone.
 template <int D>
-__device__ __forceinline__ void overflow_tile(const AttnParams& p, WaveState<D>& ws, int head, int kbase, bool partial,
-                              int lane, bf16x8_t (&pcur)[NST][2], float& l_tile) {
+__device__ __forceinline__ void overflow_tile(const AttnParams& p, WaveState<D>& ws, const bf16_t* kb, int kvh,
+                                              int kbase, bool partial, int lane, bf16x8_t (&pcur)[NST][2],
+                                              float& l_tile) {
   float mx = -INFINITY;
 #pragma unroll 1
   for (int st = 0; st < NST; ++st) {
-    const f32x16_t sc = block_scores<D>(p, ws, head, kbase, st, partial, lane);
+    const f32x16_t sc = block_scores<D>(p, ws, kb, kvh, kbase, st, partial, lane);
 #pragma unroll
     for (int r = 0; r < 16; r += 2)
       mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[r]), sc[r + 1]);
@@ -388,7 +394,7 @@ __device__ __forceinline__ void overflow_tile(const AttnParams& p, WaveState<D>&
   l_tile = 0.f;
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
-    const f32x16_t sc = block_scores<D>(p, ws, head, kbase, st, partial, lane);
+    const f32x16_t sc = block_scores<D>(p, ws, kb, kvh, kbase, st, partial, lane);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint32_t w[4];
@@ -422,8 +428,16 @@ void attn_fwd_mfma(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const int l32 = lane & 31;
-  const int head = blockIdx.x % p.n_heads;
-  const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / p.n_heads);
+  // Block -> (query tile, head slot, batch item); the slot's head keeps each
+  // group of heads that share a key/value head on one XCD (head_of_slot).
+  // All indices are block-uniform.
+  const int b = blockIdx.y;
+  const int hslot = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (unsigned)p.n_heads));
+  const int head = head_of_slot(hslot, p.xcd_heads);
+  const int kvh = __builtin_amdgcn_readfirstlane(head / p.kv_group);
+  const int qt = p.n_qtiles - 1 - __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (unsigned)p.n_heads));
+  const bf16_t* kb = p.k + (int64_t)b * p.k_bs;  // this batch item's K and V
+  const bf16_t* vb = p.v + (int64_t)b * p.v_bs;
   const int64_t nq = p.m.nq;
   const int64_t r0 = (int64_t)qt * BM;
   const int64_t rw = r0 + wave * 32;
@@ -455,7 +469,7 @@ void attn_fwd_mfma(AttnParams p) {
   // ---- Q into registers (B operand of S^T = K Q^T), rotated on load ----
   {
     uint4 raw[KSTEPS];
-    const bf16_t* src = p.q + (row_ok ? my_row : 0) * p.q_ts + (int64_t)head * p.q_hs;
+    const bf16_t* src = p.q + (int64_t)b * p.q_bs + (row_ok ? my_row : 0) * p.q_ts + (int64_t)head * p.q_hs;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
       raw[s] = row_ok ? *reinterpret_cast<const uint4*>(src + 16 * s + 8 * g) : make_uint4(0, 0, 0, 0);
@@ -484,10 +498,10 @@ void attn_fwd_mfma(AttnParams p) {
   ws.l_run = 0.f;
 
   // ---- prologue: K(0), K(1) resident, V slot 1 zeroed; S(0) computed ----
-  ld.template issue<true>(p, head, 0, kring);
+  ld.template issue<true>(p, kb, kvh, 0, kring);
   for (int i = threadIdx.x; i < L::TILE_B / 16; i += 64 * W)
     reinterpret_cast<uint4*>(vring + L::TILE_B)[i] = make_uint4(0, 0, 0, 0);
-  if (ntiles > 1) ld.template issue<true>(p, head, BN, kring + L::TILE_B);
+  if (ntiles > 1) ld.template issue<true>(p, kb, kvh, BN, kring + L::TILE_B);
   wait_vmem0();
   __syncthreads();
   f32x16_t sa[NST], sb[NST];
@@ -509,8 +523,8 @@ void attn_fwd_mfma(AttnParams p) {
   // finishes the last PV.
   auto step = [&](int j, f32x16_t (&cur)[NST], f32x16_t (&nxt)[NST], bf16x8_t (&pprev)[NST][2],
                   bf16x8_t (&pcur)[NST][2]) {
-    if (j + 2 < ntiles) ld.template issue<true>(p, head, (int64_t)(j + 2) * BN, kring + (j & 1) * L::TILE_B);
-    if (j < ntiles) ld.template issue<false>(p, head, (int64_t)j * BN, vring + (j & 1) * L::TILE_B);
+    if (j + 2 < ntiles) ld.template issue<true>(p, kb, kvh, (int64_t)(j + 2) * BN, kring + (j & 1) * L::TILE_B);
+    if (j < ntiles) ld.template issue<false>(p, vb, kvh, (int64_t)j * BN, vring + (j & 1) * L::TILE_B);
     const unsigned char* kt = kring + ((j + 1) & 1) * L::TILE_B;
     const unsigned char* vt = vring + ((j + 1) & 1) * L::TILE_B;
     const bool do_e = j < ntw;
@@ -532,7 +546,7 @@ void attn_fwd_mfma(AttnParams p) {
     // tile past the wave's keys from a stale K slot, and never uses them.
     if (j <= ntw) tile_step<D, true, true, true>(ws, kt, vt, cur, nxt, pprev, pcur, p.c_log2, l_tile);
     if (__builtin_expect(do_e && __builtin_amdgcn_ballot_w64(!(l_tile <= OVERFLOW_SUM)) != 0, 0))
-      overflow_tile<D>(p, ws, head, (int)kbase, partial, lane, pcur, l_tile);
+      overflow_tile<D>(p, ws, kb, kvh, (int)kbase, partial, lane, pcur, l_tile);
     if (do_e) ws.l_run += l_tile;
     if (j < ntiles) {
       wait_vmem0();
@@ -552,7 +566,7 @@ void attn_fwd_mfma(AttnParams p) {
   }
   if (row_ok) {
     const float inv_l = 1.f / l_run;
-    bf16_t* dst = p.o + my_row * p.o_ts + (int64_t)head * p.o_hs;
+    bf16_t* dst = p.o + (int64_t)b * p.o_bs + my_row * p.o_ts + (int64_t)head * p.o_hs;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -563,12 +577,13 @@ void attn_fwd_mfma(AttnParams p) {
         w.y = pack_bf16(ws.oacc[dt][4 * rr + 2] * inv_l, ws.oacc[dt][4 * rr + 3] * inv_l);
         *reinterpret_cast<uint2*>(dst + d0) = w;
       }
-    if (p.lse && g == 0) p.lse[(int64_t)head * nq + my_row] = (ws.m_ref + log2f(l_run)) * 0.69314718055994530942f;
+    if (p.lse && g == 0)
+      p.lse[((int64_t)b * p.n_heads + head) * nq + my_row] = (ws.m_ref + log2f(l_run)) * 0.69314718055994530942f;
   }
 }
 
 template <int D, bool RQ>
-static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
+static hipError_t launch_attn(const AttnParams& p, int n_batch, hipStream_t s) {
   constexpr int W = ATTN_WAVES;
   constexpr int BYTES = Lay<D>::BYTES;
   // Set the LDS size attribute once; concurrent first calls may both set it
@@ -580,7 +595,7 @@ static hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     configured.store(true, std::memory_order_release);
   }
-  dim3 grid((unsigned)(p.n_qtiles * p.n_heads));
+  dim3 grid((unsigned)(p.n_qtiles * p.n_heads), (unsigned)n_batch);
   hipLaunchKernelGGL((attn_fwd_mfma<D, W, RQ>), grid, dim3(64 * W), BYTES, s, p);
   return hipGetLastError();
 }
@@ -597,6 +612,14 @@ hipError_t attention_bf16_mfma(const mot_attn_args* a, const RopeTable& rt, hipS
   p.m.mode = a->mask; p.m.nq = a->nq; p.m.nk = a->nk; p.m.q0 = a->q0;
   p.m.n_ar = a->n_ar; p.m.n_prefix = a->n_prefix; p.m.chunk_len = a->chunk_len > 0 ? a->chunk_len : 1;
   p.n_heads = a->n_heads;
+  const int n_kv = a->n_kv_heads > 0 ? a->n_kv_heads : a->n_heads;
+  p.kv_group = a->n_heads / n_kv;
+  p.xcd_heads = a->n_heads % 8 == 0 ? a->n_heads / 8 : 0;
+  const int n_batch = a->n_batch > 1 ? a->n_batch : 1;
+  p.q_bs = n_batch > 1 ? a->q_bs : 0;
+  p.k_bs = n_batch > 1 ? a->k_bs : 0;
+  p.v_bs = n_batch > 1 ? a->v_bs : 0;
+  p.o_bs = n_batch > 1 ? a->o_bs : 0;
   p.n_qtiles = (int)((a->nq + 32 * ATTN_WAVES - 1) / (32 * ATTN_WAVES));
   float scale = a->scale != 0.f ? a->scale : 1.f / sqrtf((float)a->head_dim);
   p.c_log2 = scale * 1.4426950408889634f;
@@ -604,8 +627,8 @@ hipError_t attention_bf16_mfma(const mot_attn_args* a, const RopeTable& rt, hipS
   p.rope = rt;
   // K is used as given (the caller checks that no k_pos was passed)
   const bool rq = a->q_pos != nullptr;
-  if (a->head_dim == 128) return rq ? launch_attn<128, true>(p, s) : launch_attn<128, false>(p, s);
-  return rq ? launch_attn<64, true>(p, s) : launch_attn<64, false>(p, s);
+  if (a->head_dim == 128) return rq ? launch_attn<128, true>(p, n_batch, s) : launch_attn<128, false>(p, n_batch, s);
+  return rq ? launch_attn<64, true>(p, n_batch, s) : launch_attn<64, false>(p, n_batch, s);
 }
 
 }  // namespace mot

@@ -5,6 +5,8 @@
 // row holds q and its output accumulator in registers; 32-key K/V tiles are
 // staged in LDS (rotated by mRoPE while staged when key positions are given)
 // and read as broadcasts; the softmax is the streaming (online) form.
+// Grid: x = 64-row query tiles, y = heads, z = batch items; query head h
+// reads key/value head h / kv_group.
 #include "common.hpp"
 #include "rope_dev.hpp"
 
@@ -19,6 +21,8 @@ struct AttnF32Params {
   int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs;
   MaskSpec m;
   int n_heads;
+  int kv_group;
+  int64_t q_bs, k_bs, v_bs, o_bs;
   float scale;
   const float* q_pos;
   const float* k_pos;
@@ -34,12 +38,16 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(AttnF32Params p) {
   __shared__ float ks[F32_BK][D];
   __shared__ float vs[F32_BK][D];
   const int head = blockIdx.y;
+  const int kvh = head / p.kv_group;
+  const int64_t b = blockIdx.z;
+  const float* ksrc = p.k + b * p.k_bs + (int64_t)kvh * p.k_hs;  // this item's key/value head
+  const float* vsrc = p.v + b * p.v_bs + (int64_t)kvh * p.v_hs;
   const int64_t row = (int64_t)blockIdx.x * F32_BQ + threadIdx.x;
   const bool ok = row < p.m.nq;
   const int64_t i_abs = p.m.q0 + row;
 
   float q[D], o[D];
-  const float* qs = p.q + (ok ? row : 0) * p.q_ts + (int64_t)head * p.q_hs;
+  const float* qs = p.q + b * p.q_bs + (ok ? row : 0) * p.q_ts + (int64_t)head * p.q_hs;
 #pragma unroll
   for (int d = 0; d < D; ++d) { q[d] = ok ? qs[d] : 0.f; o[d] = 0.f; }
   if (p.q_pos && ok) {
@@ -65,8 +73,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(AttnF32Params p) {
       int64_t j = kb + kr;
       float kv = 0.f, vv = 0.f;
       if (j < p.m.nk) {
-        kv = p.k[j * p.k_ts + (int64_t)head * p.k_hs + d];
-        vv = p.v[j * p.v_ts + (int64_t)head * p.v_hs + d];
+        kv = ksrc[j * p.k_ts + d];
+        vv = vsrc[j * p.v_ts + d];
       }
       ks[kr][d] = kv;
       vs[kr][d] = vv;
@@ -109,10 +117,10 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(AttnF32Params p) {
   }
   if (ok) {
     float inv = 1.f / l_run;
-    float* dst = p.o + row * p.o_ts + (int64_t)head * p.o_hs;
+    float* dst = p.o + b * p.o_bs + row * p.o_ts + (int64_t)head * p.o_hs;
 #pragma unroll
     for (int d = 0; d < D; ++d) dst[d] = o[d] * inv;
-    if (p.lse) p.lse[(int64_t)head * p.m.nq + row] = m_run + logf(l_run);
+    if (p.lse) p.lse[(b * p.n_heads + head) * p.m.nq + row] = m_run + logf(l_run);
   }
 }
 
@@ -125,9 +133,15 @@ hipError_t attention_f32_valu(const mot_attn_args* a, const RopeTable& rt, hipSt
   p.m.mode = a->mask; p.m.nq = a->nq; p.m.nk = a->nk; p.m.q0 = a->q0;
   p.m.n_ar = a->n_ar; p.m.n_prefix = a->n_prefix; p.m.chunk_len = a->chunk_len > 0 ? a->chunk_len : 1;
   p.n_heads = a->n_heads;
+  p.kv_group = a->n_heads / (a->n_kv_heads > 0 ? a->n_kv_heads : a->n_heads);
+  const int n_batch = a->n_batch > 1 ? a->n_batch : 1;
+  p.q_bs = n_batch > 1 ? a->q_bs : 0;
+  p.k_bs = n_batch > 1 ? a->k_bs : 0;
+  p.v_bs = n_batch > 1 ? a->v_bs : 0;
+  p.o_bs = n_batch > 1 ? a->o_bs : 0;
   p.scale = a->scale != 0.f ? a->scale : 1.f / sqrtf((float)a->head_dim);
   p.q_pos = a->q_pos; p.k_pos = a->k_pos; p.rope = rt;
-  dim3 grid((unsigned)((a->nq + F32_BQ - 1) / F32_BQ), (unsigned)a->n_heads);
+  dim3 grid((unsigned)((a->nq + F32_BQ - 1) / F32_BQ), (unsigned)a->n_heads, (unsigned)n_batch);
   if (a->head_dim == 128)
     hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(64), 0, s, p);
   else

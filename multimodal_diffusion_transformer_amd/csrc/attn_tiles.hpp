@@ -120,4 +120,13 @@ __host__ __device__ __forceinline__ uint32_t v_read_off(int dt, int lane) {
   return (uint32_t)(rowl * Lay<D>::ROWB + ((c ^ f) * 16) + 8 * (j & 1));
 }
 
+// Head of a workgroup's head slot (blockIdx.x % n_heads).  Workgroups go
+// round-robin over the 8 XCDs; with n_heads a multiple of 8, slot hs always
+// lands on XCD hs % 8, and XCD x is given heads [x H/8, (x+1) H/8) so that
+// the query heads sharing a key/value head (consecutive heads) stay on one
+// XCD and its L2.  xcd_heads = H / 8 when H % 8 == 0, else 0 (identity).
+__host__ __device__ __forceinline__ int head_of_slot(int hs, int xcd_heads) {
+  return xcd_heads ? (hs & 7) * xcd_heads + (hs >> 3) : hs;
+}
+
 }  // namespace mot

@@ -1,11 +1,13 @@
 // Host walk of the bf16 attention kernel's tile addresses (attn_tiles.hpp):
-// every LDS-DMA copy of every K and V tile of every head, and every MFMA
-// operand read back from LDS, for a K/V view [nk][H][D] with token stride ts
-// and head stride hs (elements).  Checks, for each lane:
+// every LDS-DMA copy of every K and V tile of every key/value head of every
+// batch item, and every MFMA operand read back from LDS, for a K/V view
+// [nb][nk][H][D] with batch, token and head strides bs, ts, hs (elements)
+// inside a buffer of `extent` elements.  Checks, for each lane:
 //  * the copy's per-lane offset is the unsigned 32-bit value the kernel
 //    passes (no wrap), and scalar base + offset is exactly the element run
-//    (key, head, 8 dims) the tile row needs, with key < nk (rows past the
-//    last key re-read the last key);
+//    (key, head, 8 dims) of its batch item that the tile row needs, with
+//    key < nk (rows past the last key re-read the last key), inside the
+//    buffer;
 //  * the copy's LDS destination is the row's swizzled chunk, each 16-byte
 //    slot of the tile written once;
 //  * the K operand reads give MFMA row rho key key_perm(rho) and k-step s
@@ -36,7 +38,7 @@ static long errors = 0;
     }                                                   \
   } while (0)
 
-struct View { int64_t nk, ts, hs; int h; };
+struct View { int64_t nk, ts, hs; int h; int nb; int64_t bs, extent; };
 
 template <int D>
 struct Walk {
@@ -47,10 +49,12 @@ struct Walk {
   std::vector<int> dim;      // ... and its first dim
 
   template <bool IS_K>
-  void copy_tile(const View& v, int head, int64_t kbase) {
+  void copy_tile(const View& v, int b, int head, int64_t kbase) {
     key.assign(L::TILE_B / 16, -1);
     dim.assign(L::TILE_B / 16, -1);
-    const int64_t base_el = A::tile_base_el(kbase, v.ts, head, v.hs);
+    // the kernel offsets the tensor pointer by the batch item, then takes
+    // the tile base from it
+    const int64_t base_el = (int64_t)b * v.bs + A::tile_base_el(kbase, v.ts, head, v.hs);
     const int64_t last = v.nk - 1 - kbase;
     const uint32_t row_b = A::row_bytes(v.ts);
     CHECK((int64_t)row_b == (int64_t)L::RPI * v.ts * 2, "row bytes wrap ts=%lld", (long long)v.ts);
@@ -79,9 +83,11 @@ struct Walk {
           const int64_t k = kbase + (r > last ? last : r);
           CHECK(k >= 0 && k < v.nk, "key %lld out of range", (long long)k);
           CHECK(c >= 0 && 8 * c + 8 <= D, "chunk %d", c);
-          const int64_t want = 2 * (k * v.ts + (int64_t)head * v.hs + 8 * c);
+          const int64_t want = 2 * ((int64_t)b * v.bs + k * v.ts + (int64_t)head * v.hs + 8 * c);
           CHECK((int64_t)off == want, "address %llu != %lld (head %d kbase %lld lane %d)",
                 (unsigned long long)off, (long long)want, head, (long long)kbase, lane);
+          CHECK(want >= 0 && want / 2 + 8 <= v.extent, "outside the buffer: element %lld of %lld",
+                (long long)(want / 2), (long long)v.extent);
           const int dst = A::lds_dst(n, lane);
           CHECK(dst >= 0 && dst + 16 <= L::TILE_B, "lds dst %d", dst);
           const int srow = dst / L::ROWB, phys = (dst % L::ROWB) / 16;
@@ -151,23 +157,49 @@ struct Walk {
 
   void run(const View& v) {
     const int64_t ntiles = (v.nk + BN - 1) / BN;
-    for (int head = 0; head < v.h; ++head)
-      for (int64_t j = 0; j < ntiles; ++j) {
-        const int64_t kbase = j * BN, last = v.nk - 1 - kbase;
-        copy_tile<true>(v, head, kbase);
-        read_k(kbase, last);
-        copy_tile<false>(v, head, kbase);
-        read_v(kbase, last);
-      }
+    for (int b = 0; b < v.nb; ++b)
+      for (int head = 0; head < v.h; ++head)
+        for (int64_t j = 0; j < ntiles; ++j) {
+          const int64_t kbase = j * BN, last = v.nk - 1 - kbase;
+          copy_tile<true>(v, b, head, kbase);
+          read_k(kbase, last);
+          copy_tile<false>(v, b, head, kbase);
+          read_v(kbase, last);
+        }
   }
 };
 
+// Head slot -> head map: a bijection of the heads, and with H % 8 == 0 and
+// kv_group dividing H / 8 every group of kv_group consecutive heads (the
+// query heads of one key/value head) on a single XCD.
+static void head_map(int n_heads, int kv_group) {
+  const int xh = n_heads % 8 == 0 ? n_heads / 8 : 0;
+  std::vector<int> seen(n_heads, 0), xcd_of_kv(n_heads / kv_group, -1);
+  for (int hs = 0; hs < n_heads; ++hs) {
+    const int h = head_of_slot(hs, xh);
+    CHECK(h >= 0 && h < n_heads && !seen[h], "head map not a bijection (H %d)", n_heads);
+    if (h < 0 || h >= n_heads) continue;
+    seen[h] = 1;
+    if (xh && xh % kv_group == 0) {  // a group fits in one XCD's heads
+      int& x = xcd_of_kv[h / kv_group];
+      CHECK(x == -1 || x == hs % 8, "key/value head %d spread over XCDs", h / kv_group);
+      x = hs % 8;
+    }
+  }
+}
+
 int main(int argc, char** argv) {
-  // argv: D nk ts hs H [D nk ts hs H ...]
+  // argv: "map" H kv_group | D nk ts hs H nb bs extent, repeated
   long copies = 0, reads = 0;
-  for (int a = 1; a + 4 < argc; a += 5) {
+  int a = 1;
+  while (a + 2 < argc && argv[a][0] == 'm') {
+    head_map(atoi(argv[a + 1]), atoi(argv[a + 2]));
+    a += 3;
+  }
+  for (; a + 7 < argc; a += 8) {
     const int d = atoi(argv[a]);
-    View v{atoll(argv[a + 1]), atoll(argv[a + 2]), atoll(argv[a + 3]), atoi(argv[a + 4])};
+    View v{atoll(argv[a + 1]), atoll(argv[a + 2]), atoll(argv[a + 3]), atoi(argv[a + 4]),
+           atoi(argv[a + 5]), atoll(argv[a + 6]), atoll(argv[a + 7])};
     if (d == 128) {
       Walk<128> w;
       w.run(v);

@@ -43,8 +43,15 @@ def _build(out, inc=CSRC):
                    check=True, capture_output=True)
 
 
-def _run(exe, views):
-    args = [str(a) for v in views for a in v]
+def _full(v):
+    """(D, nk, ts, hs, H) -> one batch item in a buffer that ends at the view."""
+    d, nk, ts, hs, h = v
+    return (d, nk, ts, hs, h, 1, 0, (nk - 1) * ts + (h - 1) * hs + d)
+
+
+def _run(exe, views, maps=()):
+    args = [str(a) for m in maps for a in ("map", *m)]
+    args += [str(a) for v in views for a in (v if len(v) == 8 else _full(v))]
     r = subprocess.run([str(exe), *args], capture_output=True, text=True, timeout=600)
     return r.returncode, r.stdout
 
@@ -98,6 +105,37 @@ def test_workload_views(exe, view):
     assert rc == 0 and out.startswith("ok"), out
 
 
+def _cfg_view(wl):
+    """The guided step's K (or V) view: one packed [n_ar + n_dm + n_ar, 3, H, D]
+    buffer holding [AR cond | DM | AR base]; item 0 reads rows [0, N), item 1
+    rows [n_ar, n_ar + N)."""
+    n_ar = W.region_counts(wl.segments)[0]
+    n = wl.n_tokens
+    h, d = wl.n_heads, wl.head_dim
+    ts = 3 * h * d
+    rows = n + n_ar
+    # K starts at element h*d of the buffer; the extent is counted from there
+    return (d, n, ts, d, h, 2, n_ar * ts, rows * ts - h * d)
+
+
+@pytest.mark.parametrize("name", ["policy_bf16", "t2v480p_bf16"])
+def test_guided_pair_views(exe, name):
+    rc, out = _run(exe, [_cfg_view(W.BY_NAME[name])])
+    assert rc == 0 and out.startswith("ok"), out
+
+
+def test_grouped_heads_and_batches(exe):
+    d = 128
+    views = [
+        (d, 300, (32 + 16) * d, d, 8, 1, 0, 299 * 48 * d + 8 * d),  # 32/8-head K of a fused QKV row
+        (d, 129, 8 * d, d, 8, 3, 129 * 8 * d, 3 * 129 * 8 * d),                # 3 items, contiguous
+        (d, 70, d, 70 * d, 2, 2, 2 * 70 * d, 4 * 70 * d),                       # head-major, 2 items
+        (64, 65, 2 * 64, 64, 2, 2, 0, 64 * 64 * 2 + 64 * 2),                    # one K shared by 2 items
+    ]
+    rc, out = _run(exe, views, maps=[(24, 1), (32, 4), (16, 2), (64, 8), (8, 8), (6, 3), (40, 5)])
+    assert rc == 0 and out.startswith("ok"), out
+
+
 def test_edge_views(exe):
     rc, out = _run(exe, _edge_views())
     assert rc == 0 and out.startswith("ok"), out
@@ -115,6 +153,8 @@ PLANTED = [
     ("key_perm halves swapped", "16 * ((rho >> 2) & 1)", "16 * (1 - ((rho >> 2) & 1))"),
     ("row bytes in 16-bit arithmetic", "return (uint32_t)(L::RPI * ts * 2);",
      "return (uint32_t)(uint16_t)(L::RPI * ts * 2);"),
+    ("head slots not spread by XCD", "return xcd_heads ? (hs & 7) * xcd_heads + (hs >> 3) : hs;",
+     "return xcd_heads ? (hs % xcd_heads) * 8 + hs / xcd_heads : hs;"),
 ]
 
 
@@ -128,5 +168,5 @@ def test_planted_mistake_is_caught(tmp_path, what, pat, rep):
     out = tmp_path / "aac"
     _build(out, str(inc))
     views = [(128, 300, 9216, 128, 2), (64, 129, 768, 64, 2), (128, 70, MAX_TS, 128, 1)]
-    rc, text = _run(out, views)
+    rc, text = _run(out, views, maps=[(32, 4)])
     assert rc != 0 and "FAIL" in text, what

@@ -82,7 +82,7 @@ int main(void) {
 
 def test_header_is_strict_c99_and_cpp(tmp_path):
     src = tmp_path / "h.c"
-    src.write_text('#include "motattn.h"\nint main(void) { return mot_abi_version() == 1 ? 0 : 1; }\n')
+    src.write_text('#include "motattn.h"\nint main(void) { return mot_abi_version() == MOT_ABI_VERSION ? 0 : 1; }\n')
     for cc, std in (("gcc", "-std=c99"), ("g++", "-std=c++11")):
         r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
                             "-I", INC] + (["-x", "c++"] if cc == "g++" else []) + [str(src)],
@@ -100,7 +100,7 @@ def test_c_program_matches_the_oracle(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert out.returncode == 0, (out.returncode, out.stderr)
     lines = out.stdout.splitlines()
-    assert lines[0] == "abi 1" and lines[1] == "status1 invalid argument"
+    assert lines[0] == "abi 2" and lines[1] == "status1 invalid argument"
 
     wl = W.BY_NAME["tiny_fp32"]
     pos, reg, n_ar = olayout.build(wl.segments)

@@ -48,7 +48,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert mot.mot_abi_version() == 1
+    assert mot.mot_abi_version() == 2
     assert mot.mot_status_string(0) == "ok"
     assert "invalid" in mot.mot_status_string(1)
 
