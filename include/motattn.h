@@ -216,6 +216,20 @@ mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
 mot_status flow_euler_step(float* x, const void* v, int32_t v_dt, int64_t n,
                            float sigma, float sigma_next, void* x_bf16, void* stream);
 
+/* Guided Euler update (method page §7.2: the CFG equation and the Euler
+ * step; §7.3: both predictions of a sampler step, then one update), in place:
+ *     v    = v_base[e] + guidance * (v_cond[e] - v_base[e])
+ *     x[e] = x[e] + (sigma_next - sigma) * v,   e < n
+ * in one pass over x, v_cond and v_base.  x: device fp32; v_cond, v_base:
+ * device bf16 or fp32 (v_dt), contiguous.  In fp32: the difference, then
+ * v = fma(guidance, v_cond - v_base, v_base) and x = fma(sigma_next - sigma,
+ * v, x).  x_bf16 (nullable): also store bf16(x_new) there.  n == 0 is a
+ * no-op.  INVALID_ARG for a null or misaligned pointer, a bad v_dt or a
+ * guidance that is not finite. */
+mot_status flow_cfg_euler_step(float* x, const void* v_cond, const void* v_base, int32_t v_dt,
+                               int64_t n, float guidance, float sigma, float sigma_next,
+                               void* x_bf16, void* stream);
+
 /* Sampler noise levels with the flow shift (method page §6.3 shift map, §7.2
  * sampler loop, §12.1 recommended steps and shift per mode), host only.
  * Writes sigmas_host[k] for k = 0..n_steps into a caller-owned HOST buffer

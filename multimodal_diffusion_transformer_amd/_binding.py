@@ -30,7 +30,7 @@ MOT_AR_CAUSAL_DM_FULL, MOT_CHUNK_CAUSAL_KV = 0, 1
 EXPORTED = [
     "mot_abi_version", "mot_status_string", "mot_build_layout", "mot_qkv_project",
     "mrope_apply", "mot_attention_fwd", "flow_euler_step", "mot_mask_materialize",
-    "mot_tile_classes_host", "mot_sigma_schedule",
+    "mot_tile_classes_host", "mot_sigma_schedule", "flow_cfg_euler_step",
 ]
 
 
@@ -85,6 +85,8 @@ _lib.mot_attention_fwd.restype = ctypes.c_int
 _lib.mot_attention_fwd.argtypes = [ctypes.POINTER(mot_attn_args), _vp]
 _lib.flow_euler_step.restype = ctypes.c_int
 _lib.flow_euler_step.argtypes = [_vp, _vp, ctypes.c_int, _i64, _f32, _f32, _vp, _vp]
+_lib.flow_cfg_euler_step.restype = ctypes.c_int
+_lib.flow_cfg_euler_step.argtypes = [_vp, _vp, _vp, ctypes.c_int, _i64, _f32, _f32, _f32, _vp, _vp]
 _lib.mot_mask_materialize.restype = ctypes.c_int
 _lib.mot_mask_materialize.argtypes = [ctypes.POINTER(mot_attn_args), _vp, _i32, _i32, _vp, _vp]
 _lib.mot_tile_classes_host.restype = ctypes.c_int
@@ -249,6 +251,24 @@ def flow_euler_step(x, v, sigma, sigma_next, x_bf16=None, stream=None):
     st = _lib.flow_euler_step(_ptr(x), _ptr(v), _dtype_code(v), x.numel(), float(sigma),
                               float(sigma_next), _ptr(x_bf16), _stream(stream))
     _check("flow_euler_step", st)
+
+
+def flow_cfg_euler_step(x, v_cond, v_base, guidance, sigma, sigma_next, x_bf16=None, stream=None):
+    """x += (sigma_next - sigma) * (v_base + guidance * (v_cond - v_base))
+    over contiguous tensors (x fp32; v_cond and v_base of one dtype)."""
+    _need_cuda(x, v_cond, v_base, x_bf16)
+    import torch
+    if x.dtype != torch.float32 or not all(t.is_contiguous() for t in (x, v_cond, v_base)):
+        raise ValueError("flow_cfg_euler_step: x contiguous fp32, velocities contiguous")
+    if not (x.numel() == v_cond.numel() == v_base.numel()) or v_cond.dtype != v_base.dtype:
+        raise ValueError("flow_cfg_euler_step: sizes or velocity dtypes differ")
+    if x_bf16 is not None and (x_bf16.numel() != x.numel() or not x_bf16.is_contiguous()
+                               or x_bf16.dtype != torch.bfloat16):
+        raise ValueError("flow_cfg_euler_step: x_bf16 must be a contiguous bf16 mirror of x")
+    st = _lib.flow_cfg_euler_step(_ptr(x), _ptr(v_cond), _ptr(v_base), _dtype_code(v_cond),
+                                  x.numel(), float(guidance), float(sigma), float(sigma_next),
+                                  _ptr(x_bf16), _stream(stream))
+    _check("flow_cfg_euler_step", st)
 
 
 def mask_args(nq, nk, q0, mask, n_ar=0, n_prefix=0, chunk_len=0):

@@ -12,6 +12,12 @@ joint-attention path ("Cosmos 3 方法原理全解" §3 and §7.2):
     x = x + (sigma_next - sigma) Z_noisy, and X_noisy = bf16(x)
                                         flow_euler_step
 
+``GuidedDenoiserStep`` is a classifier-free-guided sampler step of the same
+layer (§7.2 CFG equation, §7.3 generation loop): the condition and baseline
+prompts' AR keys and values are computed once per request, and each step
+runs the DM rows only, both predictions in one attention launch, and one
+guided Euler pass.
+
 ``StreamState`` is the rolling key/value cache of the streaming mode
 ("流式生成如何工作"): [AR prefix | ring of history frame slots | current
 chunk], keys stored rotated.
@@ -40,17 +46,20 @@ class DenoiserStep:
         self.n_noisy = int((reg == 2).sum())
         self.r_noisy = self.n - self.n_noisy
         h, d, hid = wl.n_heads, wl.head_dim, wl.hidden
+        hk = getattr(wl, "n_kv_heads", 0) or h
         dt = _dt(wl.dtype)
         self.pos = torch.from_numpy(pos).to(device)
         self.X = X.to(device=device, dtype=dt).contiguous()
         self.w = [t.to(device=device, dtype=dt).contiguous() for t in (w_qkv_ar, w_qkv_dm, w_o_ar, w_o_dm)]
         self.x = x_latent.to(device=device, dtype=torch.float32).contiguous()
-        self.Y = torch.empty((self.n, 3 * h * d), dtype=dt, device=device)
+        self.Y = torch.empty((self.n, (h + 2 * hk) * d), dtype=dt, device=device)
         self.O = torch.empty((self.n, h * d), dtype=dt, device=device)
         self.Z = torch.empty((self.n, hid), dtype=dt, device=device)
         self.lse = None
-        y4 = self.Y.view(self.n, 3, h, d)
-        self.q, self.k, self.v = y4[:, 0], y4[:, 1], y4[:, 2]
+        # columns [Q (H heads) | K (H_kv) | V (H_kv)], each [heads][D]
+        self.q = self.Y[:, :h * d].view(self.n, h, d)
+        self.k = self.Y[:, h * d:(h + hk) * d].view(self.n, hk, d)
+        self.v = self.Y[:, (h + hk) * d:].view(self.n, hk, d)
         self.o3 = self.O.view(self.n, h, d)
         self.attn = B.attn_args(self.q, self.k, self.v, self.o3, mask=B.MOT_AR_CAUSAL_DM_FULL,
                                 q0=0, n_ar=n_ar, q_pos=self.pos, sections=wl.sections,
@@ -75,6 +84,103 @@ class DenoiserStep:
         B.flow_euler_step(self.x, self.Z[self.r_noisy:], sigma, sigma_next, x_bf16=mirror)
         if mirror is None:  # fp32 workloads: the next input is x itself
             self.X[self.r_noisy:].copy_(self.x)
+
+    def step(self, sigma, sigma_next):
+        self.project_qkv()
+        self.rope_k()
+        self.attention()
+        self.project_o()
+        self.euler(sigma, sigma_next)
+
+
+class GuidedDenoiserStep:
+    """Guided sampler step of the one-layer chain.
+
+    Reading: the baseline prompt takes as many AR rows as the condition
+    prompt, so the DM tokens keep their positions and, in one layer, their
+    queries, keys and values are the same in both predictions.  Every DM
+    query reads every key, so the order of its keys does not matter, and one
+    packed QKV buffer holds both predictions' keys without copies:
+
+        rows [0, n_ar)                the condition prompt's AR rows
+        rows [n_ar, n_ar + n_dm)      the DM rows of the current step
+        rows [n_ar + n_dm, N + n_ar)  the baseline prompt's AR rows
+
+    The condition prediction reads keys [0, N), the baseline prediction
+    keys [n_ar, n_ar + N); both share the DM queries.  O and Z hold the two
+    predictions' DM rows ([2, n_dm, ...]); v_cond and v_base are their noisy
+    rows.
+    """
+
+    def __init__(self, wl, X_ar_cond, X_ar_base, X_clean, w_qkv_ar, w_qkv_dm, w_o_ar, w_o_dm,
+                 x_latent, guidance, device="cuda"):
+        self.wl = wl
+        pos, reg, n_ar = B.mot_build_layout(wl.segments)
+        self.n = pos.shape[0]
+        self.n_ar = n_ar
+        self.n_dm = self.n - n_ar
+        self.n_noisy = int((reg == 2).sum())
+        self.n_clean = self.n_dm - self.n_noisy
+        self.guidance = float(guidance)
+        h, d, hid = wl.n_heads, wl.head_dim, wl.hidden
+        hk = getattr(wl, "n_kv_heads", 0) or h
+        dt = _dt(wl.dtype)
+        width = (h + 2 * hk) * d
+        self.pos = torch.from_numpy(pos).to(device)
+        self.pos_dm = self.pos[n_ar:]
+        self.w = [t.to(device=device, dtype=dt).contiguous() for t in (w_qkv_ar, w_qkv_dm, w_o_ar, w_o_dm)]
+        self.x = x_latent.to(device=device, dtype=torch.float32).contiguous()
+        rows = self.n + n_ar
+        self.QKV = torch.empty((rows, width), dtype=dt, device=device)
+        self.Xdm = torch.empty((self.n_dm, hid), dtype=dt, device=device)
+        self.Xdm[:self.n_clean].copy_(X_clean.to(device=device, dtype=dt))
+        self.Xdm[self.n_clean:].copy_(self.x.to(dt))
+        self.O = torch.empty((2, self.n_dm, h * d), dtype=dt, device=device)
+        self.Z = torch.empty((2, self.n_dm, hid), dtype=dt, device=device)
+        # per request: both prompts' AR rows through the Reasoner weights,
+        # keys rotated at the AR positions
+        a_cond = self.QKV[:n_ar]
+        a_base = self.QKV[n_ar + self.n_dm:]
+        for X_ar, dst in ((X_ar_cond, a_cond), (X_ar_base, a_base)):
+            if n_ar == 0:
+                break
+            B.mot_qkv_project(X_ar.to(device=device, dtype=dt).contiguous(), self.w[0], None, dst, n_ar)
+            B.mrope_apply(dst[:, h * d:(h + hk) * d].view(n_ar, hk, d), self.pos[:n_ar],
+                          wl.sections, wl.theta)
+        # views of the per-step buffers
+        dm = self.QKV[n_ar:n_ar + self.n_dm]
+        self.Ydm = dm
+        self.k_dm = dm[:, h * d:(h + hk) * d].view(self.n_dm, hk, d)
+        st = self.QKV.stride(0)
+        base = self.QKV.storage_offset()
+        q = dm[:, :h * d].view(self.n_dm, h, d).unsqueeze(0).expand(2, self.n_dm, h, d)
+        k = torch.as_strided(self.QKV, (2, self.n, hk, d), (n_ar * st, st, d, 1), base + h * d)
+        v = torch.as_strided(self.QKV, (2, self.n, hk, d), (n_ar * st, st, d, 1), base + (h + hk) * d)
+        o = self.O.view(2, self.n_dm, h, d)
+        # every query is a DM row (q0 = n_ar), so every key is allowed
+        self.attn = B.attn_args(q, k, v, o, mask=B.MOT_AR_CAUSAL_DM_FULL, q0=n_ar, n_ar=n_ar,
+                                q_pos=self.pos_dm, sections=wl.sections, theta=wl.theta)
+
+    def project_qkv(self):
+        B.mot_qkv_project(self.Xdm, None, self.w[1], self.Ydm, 0)
+
+    def rope_k(self):
+        B.mrope_apply(self.k_dm, self.pos_dm, self.wl.sections, self.wl.theta)
+
+    def attention(self):
+        B.mot_attention_fwd_args(self.attn)
+
+    def project_o(self):
+        B.mot_qkv_project(self.O.view(2 * self.n_dm, -1), None, self.w[3],
+                          self.Z.view(2 * self.n_dm, -1), 0)
+
+    def euler(self, sigma, sigma_next):
+        c = self.n_clean
+        mirror = self.Xdm[c:] if self.Xdm.dtype == torch.bfloat16 else None
+        B.flow_cfg_euler_step(self.x, self.Z[0, c:], self.Z[1, c:], self.guidance, sigma, sigma_next,
+                              x_bf16=mirror)
+        if mirror is None:
+            self.Xdm[c:].copy_(self.x)
 
     def step(self, sigma, sigma_next):
         self.project_qkv()

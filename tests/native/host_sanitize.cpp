@@ -209,6 +209,15 @@ static void device_argument_checks() {
   EXPECT(mot_attention_fwd(&a, NULL) == MOT_ERR_INVALID_ARG, "bad mask");
   a = attn(MOT_FP32, 64); a.q0 = INT64_MAX;
   EXPECT(mot_attention_fwd(&a, NULL) == MOT_ERR_INVALID_ARG, "q0 overflow");
+  a = attn(MOT_BF16, 128); a.n_kv_heads = 3;
+  EXPECT(mot_attention_fwd(&a, NULL) == MOT_ERR_INVALID_ARG, "kv heads not dividing");
+  a = attn(MOT_BF16, 128); a.n_batch = 70000;
+  EXPECT(mot_attention_fwd(&a, NULL) == MOT_ERR_INVALID_ARG, "batch past grid y");
+  a = attn(MOT_BF16, 128); a.n_batch = 2; a.k_bs = -256;
+  EXPECT(mot_attention_fwd(&a, NULL) == MOT_ERR_INVALID_ARG, "negative batch stride");
+  a = attn(MOT_FP32, 64); a.n_heads = 70000;
+  a.q_hs = a.k_hs = a.v_hs = a.o_hs = 64; a.q_ts = a.k_ts = a.v_ts = a.o_ts = 64 * 70000;
+  EXPECT(mot_attention_fwd(&a, NULL) == MOT_ERR_UNSUPPORTED, "fp32 heads past grid y");
 
   EXPECT(mot_qkv_project(P16, P16, P16, P16B, 10, 11, 64, 64, MOT_BF16, MOT_BF16, NULL) ==
              MOT_ERR_INVALID_ARG, "n_ar > n_rows");
@@ -240,8 +249,16 @@ static void device_argument_checks() {
          "euler empty is a no-op");
   EXPECT(flow_euler_step((float*)P_ODD, P16B, MOT_BF16, 8, 1.0f, 0.5f, NULL, NULL) == MOT_ERR_INVALID_ARG,
          "euler misaligned");
-  EXPECT(flow_euler_step((float*)P16, P16B, (mot_dtype)9, 8, 1.0f, 0.5f, NULL, NULL) == MOT_ERR_INVALID_ARG,
+  EXPECT(flow_euler_step((float*)P16, P16B, 9, 8, 1.0f, 0.5f, NULL, NULL) == MOT_ERR_INVALID_ARG,
          "euler bad dtype");
+  EXPECT(flow_cfg_euler_step((float*)P16, P16B, NULL, MOT_BF16, 8, 3.0f, 1.0f, 0.5f, NULL, NULL) ==
+             MOT_ERR_INVALID_ARG, "guided euler null base");
+  EXPECT(flow_cfg_euler_step((float*)P16, P16B, P16B, MOT_BF16, 8, NAN, 1.0f, 0.5f, NULL, NULL) ==
+             MOT_ERR_INVALID_ARG, "guided euler nan guidance");
+  EXPECT(flow_cfg_euler_step((float*)P16, P16B, P_ODD, MOT_BF16, 8, 3.0f, 1.0f, 0.5f, NULL, NULL) ==
+             MOT_ERR_INVALID_ARG, "guided euler misaligned");
+  EXPECT(flow_cfg_euler_step((float*)P16, P16B, P16B, 9, 8, 3.0f, 1.0f, 0.5f, NULL, NULL) ==
+             MOT_ERR_INVALID_ARG, "guided euler bad dtype");
 
   a = args(10, 5, 0, 0, 3, 0, 0);
   EXPECT(mot_mask_materialize(&a, (uint8_t*)P16, 128, 64, NULL, NULL) == MOT_ERR_INVALID_ARG,

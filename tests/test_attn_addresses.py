@@ -67,7 +67,8 @@ def _workload_views():
             nk = wl.stream_text + 2 + (wl.stream_history_frames + 1) * ft
             views.append((d, nk, h * d, d, h))          # the rolling cache [nk, H, D]
         else:
-            views.append((d, wl.n_tokens, 3 * h * d, d, h))  # K or V of [N, 3, H, D]
+            hk = wl.kv_heads  # K or V of the fused [N, (H + 2 H_kv) D] projection output
+            views.append((d, wl.n_tokens, (h + 2 * hk) * d, d, hk))
     return views
 
 

@@ -229,9 +229,10 @@ def test_long_480p_chain_step_sampled_rows():
     assert_parity(Z, want_z, "bf16", "o_proj long-480p")
     noisy = rows[rows >= r0]
     nt = torch.from_numpy(noisy - r0).to(dev)
+    x_in = to_np(den.x.index_select(0, nt))  # the Euler step's input
     den.euler(sig[0], sig[1])
     torch.cuda.synchronize()
-    want_x = oeuler.step(x.f32[noisy - r0], Z[rows >= r0], sig[0], sig[1])
+    want_x = oeuler.step(x_in, Z[rows >= r0], sig[0], sig[1])
     assert_parity(to_np(den.x.index_select(0, nt)), want_x, "fp32", "euler long-480p")
     # the mirror into the next step's packed input is the bf16 of x
     got_mirror = to_np(den.X.index_select(0, torch.from_numpy(noisy).to(dev)))

@@ -198,6 +198,9 @@ def _args(**kw):
     dict(mask=mot.MOT_CHUNK_CAUSAL_KV, chunk_len=8, n_prefix=10, q0=5, nk=100),
     dict(q_pos=4096, sec_t=1, sec_h=1, sec_w=1),
     dict(scale=-1.0),
+    # grouped heads: H_kv must divide H; the batch: count and strides
+    dict(n_kv_heads=3), dict(n_kv_heads=-1), dict(n_batch=-1), dict(n_batch=65536),
+    dict(n_batch=2, k_bs=-8), dict(n_batch=2, q_bs=4), dict(n_batch=2, o_bs=12),
 ])
 def test_attention_rejects_bad_args(kw):
     st = mot.raw_call("mot_attention_fwd", ctypes.byref(_args(**kw)), None)
@@ -273,3 +276,15 @@ def test_projection_and_rope_and_euler_reject_bad_args():
                         None) == mot.MOT_OK
     assert mot.raw_call("mrope_apply", None, 0, 0, 2, 128, 256, 128, None, 16, 24, 24,
                         ctypes.c_float(1e4), None) == mot.MOT_OK
+    # guided euler: a missing or unaligned velocity, a bad dtype, a guidance
+    # that is not finite; zero n is a no-op
+    f = ctypes.c_float
+    for args in [(vp(4096), vp(4096), None, 0, 64, f(3.0)), (vp(4096), vp(4096), vp(4100), 0, 64, f(3.0)),
+                 (vp(4096), vp(4096), vp(4096), 7, 64, f(3.0)),
+                 (vp(4096), vp(4096), vp(4096), 0, 64, f(float("inf"))),
+                 (vp(4096), vp(4096), vp(4096), 0, 64, f(float("nan"))),
+                 (vp(4096), vp(4096), vp(4096), 0, -1, f(3.0))]:
+        assert mot.raw_call("flow_cfg_euler_step", *args, f(1.0), f(0.5), None,
+                            None) == mot.MOT_ERR_INVALID_ARG, args
+    assert mot.raw_call("flow_cfg_euler_step", None, None, None, 0, 0, f(3.0), f(1.0), f(0.5), None,
+                        None) == mot.MOT_OK

@@ -100,6 +100,8 @@ class Workload:
     mask: int = AR_CAUSAL_DM_FULL
     sigmas: Tuple[float, ...] = ()
     theta: float = 10000.0
+    n_kv_heads: int = 0            # key/value heads (0: n_heads)
+    guidance: float = 0.0          # CFG weight of the guided step (0: unguided workload)
     # streaming (CHUNK_CAUSAL_KV) extras
     stream_views: int = 0
     stream_gh: int = 0
@@ -113,6 +115,10 @@ class Workload:
     @property
     def n_tokens(self) -> int:
         return sum(s.count() for s in self.segments)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_heads or self.n_heads
 
 
 def _linear(n_steps: int) -> Tuple[float, ...]:
@@ -168,6 +174,14 @@ def _build() -> List[Workload]:
         segments=(text(512), *eos_bog(), video(DM_CLEAN, 1, 1, 30, 52),
                   video(DM_NOISY, 48, 1, 30, 52)),
         sigmas=(1.0, 0.975)))
+    # 6. Grouped heads at the model table's Nano shape (32 query / 8 key-value
+    #    heads of 128, hidden 4096) on the 480p text-to-video layout, with the
+    #    guidance weight of the page's text-to-video settings (6).
+    w.append(Workload(
+        wid=5, name="nano_t2v480p_bf16", dtype="bf16", n_heads=32, head_dim=128,
+        hidden=4096, sections=(16, 24, 24), n_kv_heads=8, guidance=6.0,
+        segments=(text(512), *eos_bog(), video(DM_NOISY, 16, 1, 30, 52)),
+        sigmas=(1.0, 0.975)))
     return w
 
 
@@ -188,6 +202,7 @@ def region_counts(segments) -> Tuple[int, int, int]:
 # ----------------------------------------------------------------------------
 # tensor ids
 T_X, T_WQKV_AR, T_WQKV_DM, T_WO_AR, T_WO_DM, T_Q, T_K, T_V, T_LATENT = range(9)
+T_X_BASE = 9  # the baseline (negative) prompt's AR rows of a guided step
 
 
 def _rng(wid: int, tid: int, *extra: int) -> np.random.Generator:
