@@ -131,6 +131,43 @@ mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, vo
                            int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
                            int32_t in_dt, int32_t out_dt, void* stream);
 
+typedef enum { MOT_EPI_NONE = 0, MOT_EPI_GELU = 1, MOT_EPI_ADD = 2 } mot_epilogue;
+
+/* The region-split projection with an epilogue on the fp32 result, before
+ * the store (method page §3: each room has its own MLP; the layer's
+ * residual stream):
+ *     MOT_EPI_NONE  y = X W                      (= mot_qkv_project)
+ *     MOT_EPI_GELU  y = GELU(X W), GELU(v) = v (1 + erf(v / sqrt 2)) / 2
+ *                   (the MLP's first matrix)
+ *     MOT_EPI_ADD   y = residual + X W           (the output projection and
+ *                   the MLP's second matrix onto the residual stream)
+ * with W the row's room as in mot_qkv_project, and the same layouts, types,
+ * limits and errors.  residual: [n_rows, d_out] row-major of out_dt, given
+ * exactly for MOT_EPI_ADD (else NULL); it may be y itself (each element is
+ * read before it is written), but must not otherwise overlap y.
+ * INVALID_ARG for an unknown epilogue, a residual missing or given against
+ * the epilogue, or a misaligned residual. */
+mot_status mot_region_linear(const void* x, const void* w_ar, const void* w_dm, void* y,
+                             int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
+                             int32_t in_dt, int32_t out_dt, int32_t epilogue, const void* residual,
+                             void* stream);
+
+/* Region-split LayerNorm (method page §3: each room has its own LayerNorm):
+ *     y[r, :] = (x[r, :] - mean_r) / sqrt(var_r + eps) * gamma + beta
+ * over the hidden dimension, mean and (biased) variance per row in fp32,
+ * with (gamma_ar, beta_ar) for rows r < n_ar and (gamma_dm, beta_dm) for the
+ * rest.  x: [n_rows, hidden] row-major of in_dt; y: the same of out_dt (may
+ * not overlap x); gamma/beta: device fp32 [hidden].  A room with no rows may
+ * pass NULL parameters.  hidden % 8 == 0 and hidden <= 8192; eps > 0.
+ * n_rows == 0 is a no-op.  One 64-lane wave per row: n_rows * 64 <=
+ * 2^32 - 256.  INVALID_ARG for null or misaligned pointers, bad dtypes,
+ * hidden not a multiple of 8, or eps not positive and finite; UNSUPPORTED
+ * past the size limits. */
+mot_status mot_layernorm_region(const void* x, void* y, int64_t n_rows, int64_t n_ar, int64_t hidden,
+                                const float* gamma_ar, const float* beta_ar, const float* gamma_dm,
+                                const float* beta_dm, float eps, int32_t in_dt, int32_t out_dt,
+                                void* stream);
+
 /* Unified 3D mRoPE (method page §5), in place on x [n_tok][n_heads][head_dim]
  * with element strides tok_stride / head_stride (the last dim contiguous).
  * pos_thw: device float32 [n_tok][3].  Pair k of P = head_dim/2 rotates

@@ -26,11 +26,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 MOT_OK, MOT_ERR_INVALID_ARG, MOT_ERR_UNSUPPORTED, MOT_ERR_HIP = 0, 1, 2, 3
 MOT_BF16, MOT_FP32 = 0, 1
 MOT_AR_CAUSAL_DM_FULL, MOT_CHUNK_CAUSAL_KV = 0, 1
+MOT_EPI_NONE, MOT_EPI_GELU, MOT_EPI_ADD = 0, 1, 2
 
 EXPORTED = [
     "mot_abi_version", "mot_status_string", "mot_build_layout", "mot_qkv_project",
     "mrope_apply", "mot_attention_fwd", "flow_euler_step", "mot_mask_materialize",
-    "mot_tile_classes_host", "mot_sigma_schedule", "flow_cfg_euler_step",
+    "mot_tile_classes_host", "mot_sigma_schedule", "flow_cfg_euler_step", "mot_region_linear",
+    "mot_layernorm_region",
 ]
 
 
@@ -78,6 +80,12 @@ _lib.mot_build_layout.argtypes = [ctypes.POINTER(mot_segment), _i32, _i64, ctype
 _lib.mot_qkv_project.restype = ctypes.c_int
 _lib.mot_qkv_project.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
                                  ctypes.c_int, _vp]
+_lib.mot_region_linear.restype = ctypes.c_int
+_lib.mot_region_linear.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, _vp, _vp]
+_lib.mot_layernorm_region.restype = ctypes.c_int
+_lib.mot_layernorm_region.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32,
+                                      ctypes.c_int, ctypes.c_int, _vp]
 _lib.mrope_apply.restype = ctypes.c_int
 _lib.mrope_apply.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _i32,
                              _i32, _f32, _vp]
@@ -169,6 +177,36 @@ def mot_qkv_project(x, w_ar, w_dm, y, n_ar, stream=None):
     st = _lib.mot_qkv_project(_ptr(x), _ptr(w_ar), _ptr(w_dm), _ptr(y), n_rows, int(n_ar),
                               d_in, d_out, _dtype_code(x), _dtype_code(y), _stream(stream))
     _check("mot_qkv_project", st)
+
+
+def mot_region_linear(x, w_ar, w_dm, y, n_ar, epilogue=MOT_EPI_NONE, residual=None, stream=None):
+    """mot_qkv_project with an epilogue: GELU, or adding `residual` (which
+    may be y itself); contiguous row-major tensors."""
+    _need_cuda(x, w_ar, w_dm, y, residual)
+    for t in (x, w_ar, w_dm, y, residual):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("mot_region_linear takes contiguous tensors")
+    if residual is not None and (residual.shape != y.shape or residual.dtype != y.dtype):
+        raise ValueError("mot_region_linear: the residual has the output's shape and type")
+    n_rows, d_in = x.shape
+    st = _lib.mot_region_linear(_ptr(x), _ptr(w_ar), _ptr(w_dm), _ptr(y), n_rows, int(n_ar), d_in,
+                                y.shape[1], _dtype_code(x), _dtype_code(y), int(epilogue),
+                                _ptr(residual), _stream(stream))
+    _check("mot_region_linear", st)
+
+
+def mot_layernorm_region(x, y, n_ar, ln_ar, ln_dm, eps=1e-6, stream=None):
+    """Region-split LayerNorm of contiguous [N, hidden] rows; ln_ar / ln_dm
+    are (gamma, beta) fp32 device tensors (None for a room with no rows)."""
+    ln_ar = ln_ar if ln_ar is not None else (None, None)
+    ln_dm = ln_dm if ln_dm is not None else (None, None)
+    _need_cuda(x, y, *ln_ar, *ln_dm)
+    if not (x.is_contiguous() and y.is_contiguous()) or x.shape != y.shape:
+        raise ValueError("mot_layernorm_region takes contiguous [N, hidden] x and y of one shape")
+    st = _lib.mot_layernorm_region(_ptr(x), _ptr(y), x.shape[0], int(n_ar), x.shape[1], _ptr(ln_ar[0]),
+                                   _ptr(ln_ar[1]), _ptr(ln_dm[0]), _ptr(ln_dm[1]), float(eps),
+                                   _dtype_code(x), _dtype_code(y), _stream(stream))
+    _check("mot_layernorm_region", st)
 
 
 def mrope_apply(x, pos, sections, theta=10000.0, stream=None):

@@ -11,7 +11,7 @@ hipError_t attention_bf16_mfma(const mot_attn_args* a, const RopeTable& rt, hipS
 hipError_t attention_f32_valu(const mot_attn_args* a, const RopeTable& rt, hipStream_t s);
 hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* y, int64_t n_rows,
                        int64_t n_ar, int64_t K, int64_t N, mot_dtype in_dt, mot_dtype out_dt,
-                       hipStream_t s);
+                       int epi, const void* res, hipStream_t s);
 bool region_gemm_fits(int64_t n_rows, int64_t n_ar, int64_t N, mot_dtype in_dt);
 
 // One dispatch holds at most 2^32 - 1 work-items along a grid dimension.
@@ -131,9 +131,9 @@ extern "C" mot_status mot_attention_fwd(const mot_attn_args* a, void* stream) {
   return e == hipSuccess ? MOT_OK : MOT_ERR_HIP;
 }
 
-extern "C" mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, void* y,
-                                      int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
-                                      int32_t in_dt, int32_t out_dt, void* stream) {
+static mot_status region_linear(const void* x, const void* w_ar, const void* w_dm, void* y, int64_t n_rows,
+                                int64_t n_ar, int64_t d_in, int64_t d_out, int32_t in_dt, int32_t out_dt,
+                                int32_t epilogue, const void* residual, void* stream) {
   if (n_rows < 0 || n_ar < 0 || n_ar > n_rows || d_in <= 0 || d_out <= 0) return MOT_ERR_INVALID_ARG;
   if (n_rows == 0) return MOT_OK;
   if (!x || !y || (n_ar > 0 && !w_ar) || (n_ar < n_rows && !w_dm)) return MOT_ERR_INVALID_ARG;
@@ -142,10 +142,29 @@ extern "C" mot_status mot_qkv_project(const void* x, const void* w_ar, const voi
   if (((uintptr_t)x | (uintptr_t)w_ar | (uintptr_t)w_dm | (uintptr_t)y) & 15) return MOT_ERR_INVALID_ARG;
   if (in_dt == MOT_BF16 && (d_in % 64 || d_out % 64)) return MOT_ERR_UNSUPPORTED;
   if (in_dt == MOT_FP32 && out_dt != MOT_FP32) return MOT_ERR_UNSUPPORTED;
+  if (epilogue != MOT_EPI_NONE && epilogue != MOT_EPI_GELU && epilogue != MOT_EPI_ADD)
+    return MOT_ERR_INVALID_ARG;
+  if ((epilogue == MOT_EPI_ADD) != (residual != nullptr)) return MOT_ERR_INVALID_ARG;
+  if ((uintptr_t)residual & 15) return MOT_ERR_INVALID_ARG;
   if (!region_gemm_fits(n_rows, n_ar, d_out, (mot_dtype)in_dt)) return MOT_ERR_UNSUPPORTED;
   hipError_t e = region_gemm(x, w_ar, w_dm, y, n_rows, n_ar, d_in, d_out, (mot_dtype)in_dt,
-                             (mot_dtype)out_dt, (hipStream_t)stream);
+                             (mot_dtype)out_dt, epilogue, residual, (hipStream_t)stream);
   return e == hipSuccess ? MOT_OK : MOT_ERR_HIP;
+}
+
+extern "C" mot_status mot_qkv_project(const void* x, const void* w_ar, const void* w_dm, void* y,
+                                      int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
+                                      int32_t in_dt, int32_t out_dt, void* stream) {
+  return region_linear(x, w_ar, w_dm, y, n_rows, n_ar, d_in, d_out, in_dt, out_dt, MOT_EPI_NONE, nullptr,
+                       stream);
+}
+
+extern "C" mot_status mot_region_linear(const void* x, const void* w_ar, const void* w_dm, void* y,
+                                        int64_t n_rows, int64_t n_ar, int64_t d_in, int64_t d_out,
+                                        int32_t in_dt, int32_t out_dt, int32_t epilogue,
+                                        const void* residual, void* stream) {
+  return region_linear(x, w_ar, w_dm, y, n_rows, n_ar, d_in, d_out, in_dt, out_dt, epilogue, residual,
+                       stream);
 }
 
 extern "C" mot_status mot_mask_materialize(const mot_attn_args* a, uint8_t* mask_dev, int32_t bm,

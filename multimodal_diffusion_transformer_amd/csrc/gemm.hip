@@ -14,7 +14,15 @@
 // operand reads are conflict-free ds_read_b128.  Two LDS stages overlap the
 // next tile's global loads with the current MFMAs.
 // fp32 path: a plain LDS-tiled fp32 VALU GEMM.
+//
+// Epilogues on the fp32 accumulator, before the store (the rest of the MoT
+// layer, §3: each room's MLP and the residual stream): GELU, x Phi(x) in
+// its erf form, for the MLP's first matrix; or adding a residual tensor of
+// the output's type, read at exactly the offsets the store writes (so it
+// may be the output itself), for the output projection and the MLP's
+// second matrix.
 #include <atomic>
+#include <math.h>
 
 #include "common.hpp"
 
@@ -32,10 +40,15 @@ constexpr int W_ELEMS = GN * GK;
 constexpr int G_STAGE = X_ELEMS + W_ELEMS;
 constexpr int G_SMEM_BYTES = 2 * G_STAGE * 2;
 
+enum Epilogue { EPI_NONE = 0, EPI_GELU = 1, EPI_ADD = 2 };
+
+__device__ __forceinline__ float gelu_erf(float v) { return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f)); }
+
 struct GemmParams {
   const bf16_t* x;
   const bf16_t* w[2];
   void* y;
+  const void* res;     // EPI_ADD: residual, the output's type and layout
   int64_t row0[2];     // first row of each problem
   int64_t rows[2];     // rows of each problem
   int tiles_m[2];      // row tiles of each problem
@@ -103,7 +116,7 @@ __device__ inline void gemm_store_lds(bf16_t* xs, bf16_t* ws, uint4 (&xr)[4], ui
   }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(256) void gemm_region_bf16(GemmParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
@@ -180,15 +193,28 @@ __global__ __launch_bounds__(256) void gemm_region_bf16(GemmParams p) {
       for (int rr = 0; rr < 4; ++rr) {
         const int64_t n = n0 + 64 * wn + 32 * i + 8 * rr + 4 * g;
         if (n >= p.N) continue;
+        float o[4] = {acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1], acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]};
+        const int64_t e = row * p.N + n;  // the store's offset; the residual is read there too
+        if (EPI == EPI_GELU) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) o[t] = gelu_erf(o[t]);
+        } else if (EPI == EPI_ADD) {
+          if (OUT_BF16) {
+            const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.res) + e);
+            o[0] += __uint_as_float(r.x << 16); o[1] += __uint_as_float(r.x & 0xFFFF0000u);
+            o[2] += __uint_as_float(r.y << 16); o[3] += __uint_as_float(r.y & 0xFFFF0000u);
+          } else {
+            const float4 r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.res) + e);
+            o[0] += r.x; o[1] += r.y; o[2] += r.z; o[3] += r.w;
+          }
+        }
         if (OUT_BF16) {
           uint2 v;
-          v.x = g_pack_bf16(acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1]);
-          v.y = g_pack_bf16(acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.y) + row * p.N + n) = v;
+          v.x = g_pack_bf16(o[0], o[1]);
+          v.y = g_pack_bf16(o[2], o[3]);
+          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.y) + e) = v;
         } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + row * p.N + n) =
-              make_float4(acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1], acc[i][j][4 * rr + 2],
-                          acc[i][j][4 * rr + 3]);
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + e) = make_float4(o[0], o[1], o[2], o[3]);
         }
       }
   }
@@ -405,9 +431,11 @@ void gemm_region_mfma(GemmParams p) {
 // ---- fp32 VALU path ----
 constexpr int FT = 16;
 
+template <int EPI>
 __global__ __launch_bounds__(256) void gemm_region_f32(const float* x, const float* w_ar,
                                                        const float* w_dm, float* y, int64_t M,
-                                                       int64_t n_ar, int64_t K, int64_t N) {
+                                                       int64_t n_ar, int64_t K, int64_t N,
+                                                       const float* res) {
   __shared__ float xs[FT][FT + 1];
   __shared__ float wa[FT][FT + 1];
   __shared__ float wd[FT][FT + 1];
@@ -431,7 +459,11 @@ __global__ __launch_bounds__(256) void gemm_region_f32(const float* x, const flo
     for (int e = 0; e < FT; ++e) acc = __builtin_fmaf(xs[ty][e], ar ? wa[e][tx] : wd[e][tx], acc);
     __syncthreads();
   }
-  if (row < M && col < N) y[row * N + col] = acc;
+  if (row < M && col < N) {
+    if (EPI == EPI_GELU) acc = gelu_erf(acc);
+    else if (EPI == EPI_ADD) acc += res[row * N + col];
+    y[row * N + col] = acc;
+  }
 }
 
 // Whether one dispatch (at most 2^32 - 1 work-items along a grid dimension)
@@ -446,16 +478,43 @@ bool region_gemm_fits(int64_t n_rows, int64_t n_ar, int64_t N, mot_dtype in_dt) 
   return tiles_n <= lim / 256 && tiles_m <= lim / 256 / tiles_n;
 }
 
+template <bool OB>
+static hipError_t launch_bf16_gemm(const GemmParams& p, int epi, int64_t blocks, hipStream_t s) {
+  // Set the LDS size attribute once per kernel; concurrent first calls may
+  // both set it (it is idempotent), and the flag itself is atomic.
+  static std::atomic<bool> configured[3] = {{false}, {false}, {false}};
+  const void* fn = epi == EPI_GELU ? (const void*)gemm_region_bf16<OB, EPI_GELU>
+                   : epi == EPI_ADD ? (const void*)gemm_region_bf16<OB, EPI_ADD>
+                                    : (const void*)gemm_region_bf16<OB, EPI_NONE>;
+  if (!configured[epi].load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, G_SMEM_BYTES);
+    if (e != hipSuccess) return e;
+    configured[epi].store(true, std::memory_order_release);
+  }
+  const dim3 grid((unsigned)blocks), block(256);
+  if (epi == EPI_GELU) hipLaunchKernelGGL((gemm_region_bf16<OB, EPI_GELU>), grid, block, G_SMEM_BYTES, s, p);
+  else if (epi == EPI_ADD) hipLaunchKernelGGL((gemm_region_bf16<OB, EPI_ADD>), grid, block, G_SMEM_BYTES, s, p);
+  else hipLaunchKernelGGL((gemm_region_bf16<OB, EPI_NONE>), grid, block, G_SMEM_BYTES, s, p);
+  return hipGetLastError();
+}
+
 hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* y, int64_t n_rows,
                        int64_t n_ar, int64_t K, int64_t N, mot_dtype in_dt, mot_dtype out_dt,
-                       hipStream_t s) {
+                       int epi, const void* res, hipStream_t s) {
   if (in_dt == MOT_FP32) {
     dim3 grid((unsigned)((N + FT - 1) / FT), (unsigned)((n_rows + FT - 1) / FT));
-    hipLaunchKernelGGL(gemm_region_f32, grid, dim3(256), 0, s, (const float*)x,
-                       (const float*)w_ar, (const float*)w_dm, (float*)y, n_rows, n_ar, K, N);
+    const float *xf = (const float*)x, *wa = (const float*)w_ar, *wd = (const float*)w_dm;
+    const float* rf = (const float*)res;
+    if (epi == EPI_GELU)
+      hipLaunchKernelGGL(gemm_region_f32<EPI_GELU>, grid, dim3(256), 0, s, xf, wa, wd, (float*)y, n_rows, n_ar, K, N, rf);
+    else if (epi == EPI_ADD)
+      hipLaunchKernelGGL(gemm_region_f32<EPI_ADD>, grid, dim3(256), 0, s, xf, wa, wd, (float*)y, n_rows, n_ar, K, N, rf);
+    else
+      hipLaunchKernelGGL(gemm_region_f32<EPI_NONE>, grid, dim3(256), 0, s, xf, wa, wd, (float*)y, n_rows, n_ar, K, N, rf);
     return hipGetLastError();
   }
   GemmParams p;
+  p.res = res;
   p.x = (const bf16_t*)x;
   p.w[0] = (const bf16_t*)w_ar;
   p.w[1] = (const bf16_t*)w_dm;
@@ -464,7 +523,7 @@ hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* 
   p.row0[1] = n_ar; p.rows[1] = n_rows - n_ar;
   p.K = K; p.N = N;
 #if defined(MOT_GEMM_DMA) && MOT_GEMM_DMA
-  if (K % HK == 0 && N % 64 == 0) {  // direct-to-LDS MFMA kernel
+  if (K % HK == 0 && N % 64 == 0 && epi == EPI_NONE) {  // direct-to-LDS MFMA kernel
     const int ob = out_dt == MOT_BF16 ? 1 : 0;
     p.tiles_m[0] = (int)((p.rows[0] + HM - 1) / HM);
     p.tiles_m[1] = (int)((p.rows[1] + HM - 1) / HM);
@@ -490,21 +549,7 @@ hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* 
   p.tiles_n = (int)((N + GN - 1) / GN);
   const int64_t blocks = (int64_t)(p.tiles_m[0] + p.tiles_m[1]) * p.tiles_n;
   if (blocks == 0) return hipSuccess;
-  // Set the LDS size attribute once; concurrent first calls may both set it
-  // (it is idempotent), and the flag itself is atomic.
-  static std::atomic<bool> configured[2] = {{false}, {false}};
-  const int ob = out_dt == MOT_BF16 ? 1 : 0;
-  const void* fn = ob ? (const void*)gemm_region_bf16<true> : (const void*)gemm_region_bf16<false>;
-  if (!configured[ob].load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, G_SMEM_BYTES);
-    if (e != hipSuccess) return e;
-    configured[ob].store(true, std::memory_order_release);
-  }
-  if (ob)
-    hipLaunchKernelGGL(gemm_region_bf16<true>, dim3((unsigned)blocks), dim3(256), G_SMEM_BYTES, s, p);
-  else
-    hipLaunchKernelGGL(gemm_region_bf16<false>, dim3((unsigned)blocks), dim3(256), G_SMEM_BYTES, s, p);
-  return hipGetLastError();
+  return out_dt == MOT_BF16 ? launch_bf16_gemm<true>(p, epi, blocks, s) : launch_bf16_gemm<false>(p, epi, blocks, s);
 }
 
 }  // namespace mot

@@ -18,6 +18,17 @@ prompts' AR keys and values are computed once per request, and each step
 runs the DM rows only, both predictions in one attention launch, and one
 guided Euler pass.
 
+``BlockStep`` is the whole MoT layer (§3: each room has its own LayerNorm,
+QKV, output projection and MLP) over the packed rows:
+
+    U1 = LN1(X)                         mot_layernorm_region
+    Y  = QKV(U1); K = mRoPE(K)          mot_qkv_project, mrope_apply
+    O  = attention                      mot_attention_fwd (Q rotated on load)
+    H1 = X + Oproj(O)                   mot_region_linear (residual add)
+    U2 = LN2(H1)                        mot_layernorm_region
+    A  = GELU(U2 W_up)                  mot_region_linear (GELU)
+    H2 = H1 + A W_down                  mot_region_linear (residual add)
+
 ``StreamState`` is the rolling key/value cache of the streaming mode
 ("流式生成如何工作"): [AR prefix | ring of history frame slots | current
 chunk], keys stored rotated.
@@ -188,6 +199,70 @@ class GuidedDenoiserStep:
         self.attention()
         self.project_o()
         self.euler(sigma, sigma_next)
+
+
+class BlockStep:
+    """The whole MoT layer's forward over one packed block of rows."""
+
+    def __init__(self, wl, X, params, device="cuda", eps=1e-6):
+        """X: [N, hidden] packed rows; params: oracle.block's keys, each a
+        torch tensor or a (gamma, beta) pair of fp32 tensors."""
+        self.wl = wl
+        pos, reg, n_ar = B.mot_build_layout(wl.segments)
+        self.n, self.n_ar, self.eps = pos.shape[0], n_ar, eps
+        h, d, hid, ffn = wl.n_heads, wl.head_dim, wl.hidden, wl.ffn
+        hk = getattr(wl, "n_kv_heads", 0) or h
+        dt = _dt(wl.dtype)
+        n = self.n
+        dev = lambda t, ty: t.to(device=device, dtype=ty).contiguous()
+        self.p = {}
+        for k, v in params.items():
+            self.p[k] = tuple(dev(t, torch.float32) for t in v) if k.startswith("ln") else dev(v, dt)
+        self.pos = torch.from_numpy(pos).to(device)
+        self.X = dev(X, dt)
+        self.U = torch.empty((n, hid), dtype=dt, device=device)
+        self.Y = torch.empty((n, (h + 2 * hk) * d), dtype=dt, device=device)
+        self.O = torch.empty((n, h * d), dtype=dt, device=device)
+        self.H1 = torch.empty((n, hid), dtype=dt, device=device)
+        self.A = torch.empty((n, ffn), dtype=dt, device=device)
+        self.H2 = torch.empty((n, hid), dtype=dt, device=device)
+        self.q = self.Y[:, :h * d].view(n, h, d)
+        self.k = self.Y[:, h * d:(h + hk) * d].view(n, hk, d)
+        self.v = self.Y[:, (h + hk) * d:].view(n, hk, d)
+        self.attn = B.attn_args(self.q, self.k, self.v, self.O.view(n, h, d),
+                                mask=B.MOT_AR_CAUSAL_DM_FULL, q0=0, n_ar=n_ar, q_pos=self.pos,
+                                sections=wl.sections, theta=wl.theta)
+
+    def ln1(self):
+        B.mot_layernorm_region(self.X, self.U, self.n_ar, self.p["ln1_ar"], self.p["ln1_dm"], self.eps)
+
+    def project_qkv(self):
+        B.mot_qkv_project(self.U, self.p["qkv_ar"], self.p["qkv_dm"], self.Y, self.n_ar)
+
+    def rope_k(self):
+        B.mrope_apply(self.k, self.pos, self.wl.sections, self.wl.theta)
+
+    def attention(self):
+        B.mot_attention_fwd_args(self.attn)
+
+    def project_o(self):
+        B.mot_region_linear(self.O, self.p["o_ar"], self.p["o_dm"], self.H1, self.n_ar,
+                            B.MOT_EPI_ADD, residual=self.X)
+
+    def ln2(self):
+        B.mot_layernorm_region(self.H1, self.U, self.n_ar, self.p["ln2_ar"], self.p["ln2_dm"], self.eps)
+
+    def mlp_up(self):
+        B.mot_region_linear(self.U, self.p["up_ar"], self.p["up_dm"], self.A, self.n_ar, B.MOT_EPI_GELU)
+
+    def mlp_down(self):
+        B.mot_region_linear(self.A, self.p["down_ar"], self.p["down_dm"], self.H2, self.n_ar,
+                            B.MOT_EPI_ADD, residual=self.H1)
+
+    def forward(self):
+        for f in (self.ln1, self.project_qkv, self.rope_k, self.attention, self.project_o,
+                  self.ln2, self.mlp_up, self.mlp_down):
+            f()
 
 
 class StreamState:

@@ -44,6 +44,27 @@ def assert_parity(got, want, dtype="bf16", what=""):
     return ma, rl
 
 
+def bf16_spacing(v):
+    """One bfloat16 spacing at |v| (8 significant bits), elementwise."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 7), 0.0)
+
+
+def assert_parity_stored(got, want, what=""):
+    """The bf16 contract for a tensor stored in bf16 whose values may be
+    large: relative L2 <= 5e-3, and per element |got - want| <=
+    max(2e-2, one bf16 spacing of want).  Storing a value in bf16 moves it
+    by up to half a spacing, which passes 2e-2 once |value| >= 8 (and two
+    stored results may sit a spacing apart from |value| >= 4)."""
+    ma, rl = errors(got, want)
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
+    worst = float((d / np.maximum(BF16_MAX_ABS, bf16_spacing(want))).max()) if d.size else 0.0
+    say("  parity %-28s max_abs=%.3e rel_l2=%.3e worst/allowance=%.2f (stored bf16)" % (what, ma, rl, worst))
+    assert rl <= BF16_REL_L2 and worst <= 1.0, (what, ma, rl, worst)
+    return ma, rl
+
+
 def to_np(t):
     from workloads import to_numpy_f32
     return to_numpy_f32(t)

@@ -260,6 +260,23 @@ static void device_argument_checks() {
   EXPECT(flow_cfg_euler_step((float*)P16, P16B, P16B, 9, 8, 3.0f, 1.0f, 0.5f, NULL, NULL) ==
              MOT_ERR_INVALID_ARG, "guided euler bad dtype");
 
+  EXPECT(mot_region_linear(P16, P16, P16, P16B, 10, 5, 64, 64, MOT_BF16, MOT_BF16, 7, NULL, NULL) ==
+             MOT_ERR_INVALID_ARG, "unknown epilogue");
+  EXPECT(mot_region_linear(P16, P16, P16, P16B, 10, 5, 64, 64, MOT_BF16, MOT_BF16, MOT_EPI_ADD, NULL, NULL) ==
+             MOT_ERR_INVALID_ARG, "add without residual");
+  EXPECT(mot_region_linear(P16, P16, P16, P16B, 10, 5, 64, 64, MOT_BF16, MOT_BF16, MOT_EPI_GELU, P16, NULL) ==
+             MOT_ERR_INVALID_ARG, "residual without add");
+  EXPECT(mot_layernorm_region(P16, P16B, 10, 4, 100, (const float*)P16, (const float*)P16,
+                              (const float*)P16, (const float*)P16, 1e-6f, MOT_BF16, MOT_BF16, NULL) ==
+             MOT_ERR_INVALID_ARG, "layernorm hidden");
+  EXPECT(mot_layernorm_region(P16, P16B, 10, 4, 64, (const float*)P16, (const float*)P16, NULL, NULL, 1e-6f,
+                              MOT_BF16, MOT_BF16, NULL) == MOT_ERR_INVALID_ARG, "layernorm DM rows, no params");
+  EXPECT(mot_layernorm_region(P16, P16B, 10, 4, 64, (const float*)P16, (const float*)P16, (const float*)P16,
+                              (const float*)P16, -1.0f, MOT_BF16, MOT_BF16, NULL) == MOT_ERR_INVALID_ARG,
+         "layernorm eps");
+  EXPECT(mot_layernorm_region(P16, P16B, (int64_t)1 << 40, 4, 64, (const float*)P16, (const float*)P16,
+                              (const float*)P16, (const float*)P16, 1e-6f, MOT_BF16, MOT_BF16, NULL) ==
+             MOT_ERR_UNSUPPORTED, "layernorm dispatch too large");
   a = args(10, 5, 0, 0, 3, 0, 0);
   EXPECT(mot_mask_materialize(&a, (uint8_t*)P16, 128, 64, NULL, NULL) == MOT_ERR_INVALID_ARG,
          "mask invalid args");

@@ -288,3 +288,23 @@ def test_projection_and_rope_and_euler_reject_bad_args():
                             None) == mot.MOT_ERR_INVALID_ARG, args
     assert mot.raw_call("flow_cfg_euler_step", None, None, None, 0, 0, f(3.0), f(1.0), f(0.5), None,
                         None) == mot.MOT_OK
+    # region linear: unknown epilogue, residual missing for ADD or given
+    # otherwise, misaligned residual; empty is a no-op
+    P = vp(4096)
+    for epi, res in [(3, None), (-1, None), (mot.MOT_EPI_ADD, None), (mot.MOT_EPI_GELU, P),
+                     (mot.MOT_EPI_NONE, P), (mot.MOT_EPI_ADD, vp(4100))]:
+        assert mot.raw_call("mot_region_linear", P, P, P, P, 10, 5, 64, 64, 0, 0, epi, res,
+                            None) == mot.MOT_ERR_INVALID_ARG, (epi, res)
+    assert mot.raw_call("mot_region_linear", None, None, None, None, 0, 0, 64, 64, 0, 0,
+                        mot.MOT_EPI_GELU, None, None) == mot.MOT_OK
+    # layernorm: hidden not a multiple of 8, eps not positive, a room with
+    # rows but no parameters, misaligned, too wide; empty is a no-op
+    for args in [(10, 4, 100, P, P, P, P, f(1e-6)), (10, 4, 64, P, P, P, P, f(0.0)),
+                 (10, 4, 64, P, P, P, P, f(float("nan"))), (10, 4, 64, None, P, P, P, f(1e-6)),
+                 (10, 4, 64, P, P, None, None, f(1e-6)), (10, 4, 64, P, vp(4100), P, P, f(1e-6))]:
+        assert mot.raw_call("mot_layernorm_region", P, P, *args, 0, 0, None) == \
+            mot.MOT_ERR_INVALID_ARG, args
+    assert mot.raw_call("mot_layernorm_region", P, P, 10, 4, 8200, P, P, P, P, f(1e-6), 0, 0,
+                        None) == mot.MOT_ERR_UNSUPPORTED
+    assert mot.raw_call("mot_layernorm_region", None, None, 0, 0, 64, None, None, None, None,
+                        f(1e-6), 0, 0, None) == mot.MOT_OK

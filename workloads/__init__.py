@@ -101,6 +101,7 @@ class Workload:
     sigmas: Tuple[float, ...] = ()
     theta: float = 10000.0
     n_kv_heads: int = 0            # key/value heads (0: n_heads)
+    ffn: int = 0                   # MLP width of the whole layer (0: the attention path only)
     guidance: float = 0.0          # CFG weight of the guided step (0: unguided workload)
     # streaming (CHUNK_CAUSAL_KV) extras
     stream_views: int = 0
@@ -179,7 +180,7 @@ def _build() -> List[Workload]:
     #    guidance weight of the page's text-to-video settings (6).
     w.append(Workload(
         wid=5, name="nano_t2v480p_bf16", dtype="bf16", n_heads=32, head_dim=128,
-        hidden=4096, sections=(16, 24, 24), n_kv_heads=8, guidance=6.0,
+        hidden=4096, sections=(16, 24, 24), n_kv_heads=8, guidance=6.0, ffn=12288,
         segments=(text(512), *eos_bog(), video(DM_NOISY, 16, 1, 30, 52)),
         sigmas=(1.0, 0.975)))
     return w
@@ -203,6 +204,10 @@ def region_counts(segments) -> Tuple[int, int, int]:
 # tensor ids
 T_X, T_WQKV_AR, T_WQKV_DM, T_WO_AR, T_WO_DM, T_Q, T_K, T_V, T_LATENT = range(9)
 T_X_BASE = 9  # the baseline (negative) prompt's AR rows of a guided step
+# the whole layer: LayerNorm gamma / beta of each room (ln1, ln2), MLP matrices
+T_LN1_G_AR, T_LN1_B_AR, T_LN1_G_DM, T_LN1_B_DM = 10, 11, 12, 13
+T_LN2_G_AR, T_LN2_B_AR, T_LN2_G_DM, T_LN2_B_DM = 14, 15, 16, 17
+T_UP_AR, T_UP_DM, T_DOWN_AR, T_DOWN_DM = 18, 19, 20, 21
 
 
 def _rng(wid: int, tid: int, *extra: int) -> np.random.Generator:
@@ -242,6 +247,34 @@ def make(wid: int, tid: int, shape, dtype: str, std: float = 1.0, *extra: int) -
         b = bf16_bits(x)
         return Tensor("bf16", b, bf16_to_f32(b))
     return Tensor("fp32", x, x)
+
+
+def block_params(wl: Workload, dtype: Optional[str] = None) -> dict:
+    """Seeded parameters of the whole layer for workload wl: LayerNorm gamma
+    ~ 1 + N(0, 0.1^2) and beta ~ N(0, 0.1^2) (fp32), projection and MLP
+    matrices ~ N(0, 0.02^2) in the workload's dtype.  Keys as oracle.block
+    takes them; the (gamma, beta) pairs and matrices are Tensors."""
+    dt = dtype or wl.dtype
+    h, d, hid, hk, ffn = wl.n_heads, wl.head_dim, wl.hidden, wl.kv_heads, wl.ffn
+    width = (h + 2 * hk) * d
+
+    def ln(tg, tb):
+        g = make(wl.wid, tg, (hid,), "fp32", 0.1)
+        g = Tensor("fp32", g.f32 + np.float32(1.0), g.f32 + np.float32(1.0))
+        return g, make(wl.wid, tb, (hid,), "fp32", 0.1)
+
+    return {
+        "ln1_ar": ln(T_LN1_G_AR, T_LN1_B_AR), "ln1_dm": ln(T_LN1_G_DM, T_LN1_B_DM),
+        "ln2_ar": ln(T_LN2_G_AR, T_LN2_B_AR), "ln2_dm": ln(T_LN2_G_DM, T_LN2_B_DM),
+        "qkv_ar": make(wl.wid, T_WQKV_AR, (hid, width), dt, 0.02),
+        "qkv_dm": make(wl.wid, T_WQKV_DM, (hid, width), dt, 0.02),
+        "o_ar": make(wl.wid, T_WO_AR, (h * d, hid), dt, 0.02),
+        "o_dm": make(wl.wid, T_WO_DM, (h * d, hid), dt, 0.02),
+        "up_ar": make(wl.wid, T_UP_AR, (hid, ffn), dt, 0.02),
+        "up_dm": make(wl.wid, T_UP_DM, (hid, ffn), dt, 0.02),
+        "down_ar": make(wl.wid, T_DOWN_AR, (ffn, hid), dt, 0.02),
+        "down_dm": make(wl.wid, T_DOWN_DM, (ffn, hid), dt, 0.02),
+    }
 
 
 def to_torch(t: Tensor, device=None):
