@@ -205,8 +205,9 @@ class BlockStep:
     """The whole MoT layer's forward over one packed block of rows."""
 
     def __init__(self, wl, X, params, device="cuda", eps=1e-6):
-        """X: [N, hidden] packed rows; params: oracle.block's keys, each a
-        torch tensor or a (gamma, beta) pair of fp32 tensors."""
+        """X: [N, hidden] packed rows; params: ln1_ar, ln1_dm, ln2_ar, ln2_dm
+        ((gamma, beta) pairs of fp32 tensors) and qkv_ar, qkv_dm, o_ar, o_dm,
+        up_ar, up_dm, down_ar, down_dm (matrices [d_in, d_out])."""
         self.wl = wl
         pos, reg, n_ar = B.mot_build_layout(wl.segments)
         self.n, self.n_ar, self.eps = pos.shape[0], n_ar, eps
