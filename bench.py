@@ -208,6 +208,12 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="t2v480p_bf16")
+    ap.add_argument("--mode", default="step", choices=["step", "guided", "block"],
+                    help="step: one sampler step of the one-layer chain (the default line); guided: "
+                         "a classifier-free-guided step (both predictions in one attention launch, "
+                         "fused guided Euler); block: the whole MoT layer forward (LayerNorms, "
+                         "projections, attention, GELU MLP, residuals; needs a workload with an MLP "
+                         "width)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -252,21 +258,44 @@ def main():
         return bench_stream(args, wl)
     dev = torch.device("cuda:0")
     n, hid, h, d = wl.n_tokens, wl.hidden, wl.n_heads, wl.head_dim
+    hk = wl.kv_heads
     n_ar, n_clean, n_noisy = W.region_counts(wl.segments)
     X = W.make(wl.wid, W.T_X, (n, hid), wl.dtype)
-    ws = [W.make(wl.wid, W.T_WQKV_AR, (hid, 3 * h * d), wl.dtype, 0.02),
-          W.make(wl.wid, W.T_WQKV_DM, (hid, 3 * h * d), wl.dtype, 0.02),
-          W.make(wl.wid, W.T_WO_AR, (h * d, hid), wl.dtype, 0.02),
-          W.make(wl.wid, W.T_WO_DM, (h * d, hid), wl.dtype, 0.02)]
-    x = W.make(wl.wid, W.T_LATENT, (n_noisy, hid), "fp32")
-    den = pipeline.DenoiserStep(wl, W.to_torch(X), *(W.to_torch(w) for w in ws),
-                                torch.from_numpy(x.f32), device=dev)
-    del X, ws, x
-    sig = (1.0, 0.975)
-
-    stages = ["qkv", "rope_k", "attention", "o_proj", "euler"]
-    fns = [den.project_qkv, den.rope_k, den.attention, den.project_o,
-           lambda: den.euler(*sig)]
+    sig = tuple(wl.sigmas[:2])  # the workload's first sampler step
+    if args.mode == "block":
+        if not wl.ffn:
+            raise SystemExit("--mode block needs a workload with an MLP width (e.g. nano_t2v480p_bf16)")
+        params = W.block_params(wl)
+        tp = {k: (tuple(W.to_torch(t) for t in v) if k.startswith("ln") else W.to_torch(v))
+              for k, v in params.items()}
+        blk = pipeline.BlockStep(wl, W.to_torch(X), tp, device=dev)
+        del X, params, tp
+        stages = ["ln1", "qkv", "rope_k", "attention", "o_proj_residual", "ln2", "mlp_up_gelu",
+                  "mlp_down_residual"]
+        fns = [blk.ln1, blk.project_qkv, blk.rope_k, blk.attention, blk.project_o, blk.ln2,
+               blk.mlp_up, blk.mlp_down]
+    else:
+        width = (h + 2 * hk) * d
+        ws = [W.make(wl.wid, W.T_WQKV_AR, (hid, width), wl.dtype, 0.02),
+              W.make(wl.wid, W.T_WQKV_DM, (hid, width), wl.dtype, 0.02),
+              W.make(wl.wid, W.T_WO_AR, (h * d, hid), wl.dtype, 0.02),
+              W.make(wl.wid, W.T_WO_DM, (h * d, hid), wl.dtype, 0.02)]
+        x = W.make(wl.wid, W.T_LATENT, (n_noisy, hid), "fp32")
+        if args.mode == "guided":
+            Xb = W.make(wl.wid, W.T_X_BASE, (n_ar, hid), wl.dtype)
+            Xt = W.to_torch(X)
+            den = pipeline.GuidedDenoiserStep(wl, Xt[:n_ar], W.to_torch(Xb), Xt[n_ar:n_ar + n_clean],
+                                              *(W.to_torch(w) for w in ws), torch.from_numpy(x.f32),
+                                              wl.guidance or 6.0, device=dev)
+            stages = ["qkv_dm", "rope_k_dm", "attention_pair", "o_proj_pair", "cfg_euler"]
+            del Xb, Xt
+        else:
+            den = pipeline.DenoiserStep(wl, W.to_torch(X), *(W.to_torch(w) for w in ws),
+                                        torch.from_numpy(x.f32), device=dev)
+            stages = ["qkv", "rope_k", "attention", "o_proj", "euler"]
+        del X, ws, x
+        fns = [den.project_qkv, den.rope_k, den.attention, den.project_o,
+               lambda: den.euler(*sig)]
 
     def step(ev=None):
         for i, f in enumerate(fns):
@@ -292,10 +321,19 @@ def main():
            for i, name in enumerate(stages)}
     ms_step = wall * 1e3 / args.steps
 
-    pairs = attention_pairs(n, n_ar)
+    attn_stage = [k for k in stages if k.startswith("attention")][0]
+    if args.mode == "guided":
+        # DM queries only, two predictions, every key allowed
+        pairs = 2 * (n - n_ar) * n
+        rows_proj = n - n_ar
+        proj_flops = 2.0 * rows_proj * hid * (h + 2 * hk) * d + 2.0 * 2 * rows_proj * h * d * hid
+    else:
+        pairs = attention_pairs(n, n_ar)
+        proj_flops = 2.0 * n * hid * (h + 2 * hk) * d + 2.0 * n * h * d * hid
+        if args.mode == "block":
+            proj_flops += 2.0 * 2 * n * hid * wl.ffn
     attn_flops = 4.0 * d * h * pairs
-    proj_flops = 2.0 * n * hid * 3 * h * d + 2.0 * n * h * d * hid
-    attn_tflops = attn_flops / (per["attention"] * 1e-3) / 1e12
+    attn_tflops = attn_flops / (per[attn_stage] * 1e-3) / 1e12
     value = attn_flops / (ms_step * 1e-3) / 1e12
     line = {
         "metric": "MoT masked-attention TFLOP/s (unmasked pairs) + % of MI355X bf16 MFMA peak",
@@ -312,11 +350,16 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights, random init)",
         "config": {"workload": "%s: T2V 480p-shaped packed sequence, %d AR (512 text + EOS + BOG)"
                                " + %d DM-noisy (16 latent frames x 30x52), %d heads x %d, hidden %d"
-                               % (wl.name, n_ar, n_noisy, h, d, hid) if wl.name == "t2v480p_bf16"
-                   else wl.name,
+                               % (wl.name, n_ar, n_noisy, h, d, hid)
+                               if wl.name == "t2v480p_bf16" and args.mode == "step" else wl.name,
                    "tokens": n, "n_ar": n_ar, "n_clean": n_clean, "n_noisy": n_noisy,
-                   "heads": h, "head_dim": d, "hidden": hid, "mask": "AR_CAUSAL_DM_FULL",
-                   "step": "qkv_proj + mrope(K; Q on load) + attention + o_proj + euler"},
+                   "heads": h, "kv_heads": hk, "head_dim": d, "hidden": hid, "mask": "AR_CAUSAL_DM_FULL",
+                   "step": {"step": "qkv_proj + mrope(K; Q on load) + attention + o_proj + euler",
+                            "guided": "DM rows: qkv_proj + mrope(K) + attention of both predictions "
+                                      "in one launch + o_proj of both + guided euler (w=%g)"
+                                      % (wl.guidance or 6.0),
+                            "block": "ln1 + qkv_proj + mrope(K) + attention + o_proj(+residual) + "
+                                     "ln2 + mlp_up(gelu) + mlp_down(+residual), FFN %d" % wl.ffn}[args.mode]},
         "pct_of_peak_step": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "attention_kernel_tflops": round(attn_tflops, 2),
         "step_tflops_all_contractions": round((attn_flops + proj_flops) / (ms_step * 1e-3) / 1e12, 2),
@@ -324,7 +367,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic_from_profile(wl.name)},
+                     "traffic": traffic_from_profile(wl.name) if args.mode == "step" else None},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
