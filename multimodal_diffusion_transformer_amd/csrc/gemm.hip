@@ -25,6 +25,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "gemm_tiles.hpp"
 
 namespace mot {
 
@@ -238,14 +239,8 @@ __global__ __launch_bounds__(256) void gemm_region_bf16(GemmParams p) {
 //    read with ds_read_b128.
 // Both reads are bank-conflict free.  The next stage's copies are issued at
 // the start of a stage and waited for at its end; inside a stage the second
-// k-step's operands are read under the first k-step's MFMAs.
-constexpr int HM = 256;   // rows per workgroup
-constexpr int HN = 128;   // cols per workgroup
-constexpr int HK = 32;    // depth per stage
-constexpr int H_WB = HK * HN * 2;             // W tile bytes (8 KB)
-constexpr int H_XB = HM * HK * 2;             // X tile bytes (16 KB)
-constexpr int H_STAGE = H_WB + H_XB;          // 24 KB
-constexpr int H_SMEM_BYTES = 2 * H_STAGE;     // 48 KB
+// k-step's operands are read under the first k-step's MFMAs.  The tile
+// geometry and every address are GemmTileAddr's (gemm_tiles.hpp).
 static_assert(H_SMEM_BYTES <= 65536, "LDS copies stay below 64 KB");
 
 // One wave-wide 16-byte-per-lane copy from global memory (scalar base +
@@ -277,35 +272,27 @@ typedef __attribute__((address_space(3))) g_s16x4_t g_lds_s16x4_t;
 __device__ __forceinline__ void h_issue(const GemmParams& p, const bf16_t* w, int64_t r0, int64_t rows,
                                         int64_t n0, int64_t k0, int wave, int lane, uint32_t lw,
                                         uint32_t lx, unsigned char* dst) {
+  using A = GemmTileAddr;
   const int64_t N = p.N, K = p.K;
-  const char* wb = reinterpret_cast<const char*>(w) + (k0 * N + n0) * 2;
+  const char* wb = reinterpret_cast<const char*>(w) + A::w_tile_el(k0, n0, N) * 2;
   const bool ragged_n = n0 + HN > N;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int i = 2 * wave + t;  // rows 4i .. 4i+3 of the W tile
-    if (__builtin_expect(!ragged_n, 1)) {
-      g_dma16(wb + (int64_t)4 * i * N * 2, lw, g_lds_addr(dst + i * 1024));
-    } else {
-      const int row = 4 * i + lane / 16;
-      int c = (lane % 16) ^ (4 * (row & 3));  // logical chunk of this lane's slot
-      const int last_c = (int)((N - n0) / 8) - 1;
-      if (c > last_c) c = last_c;
-      g_dma16(wb, (uint32_t)((int64_t)row * N * 2 + c * 16), g_lds_addr(dst + i * 1024));
-    }
+    const int i = A::w_load(wave, t);
+    if (__builtin_expect(!ragged_n, 1))
+      g_dma16(wb + A::w_load_bytes(i, N), lw, g_lds_addr(dst + A::w_lds(i, 0)));
+    else
+      g_dma16(wb, A::w_ragged_off(i, lane, N, n0), g_lds_addr(dst + A::w_lds(i, 0)));
   }
-  const char* xb = reinterpret_cast<const char*>(p.x) + (r0 * K + k0) * 2;
+  const char* xb = reinterpret_cast<const char*>(p.x) + A::x_tile_el(r0, k0, K) * 2;
   const bool ragged_m = rows < HM;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int i = 4 * wave + t;  // rows 16i .. 16i+15 of the X tile
-    if (__builtin_expect(!ragged_m, 1)) {
-      g_dma16(xb + (int64_t)16 * i * K * 2, lx, g_lds_addr(dst + H_WB + i * 1024));
-    } else {
-      int64_t row = 16 * i + lane / 4;
-      const int c = (lane % 4) ^ ((int)(row >> 2) & 1);
-      if (row > rows - 1) row = rows - 1;
-      g_dma16(xb, (uint32_t)(row * K * 2 + c * 16), g_lds_addr(dst + H_WB + i * 1024));
-    }
+    const int i = A::x_load(wave, t);
+    if (__builtin_expect(!ragged_m, 1))
+      g_dma16(xb + A::x_load_bytes(i, K), lx, g_lds_addr(dst + A::x_lds(i, 0)));
+    else
+      g_dma16(xb, A::x_ragged_off(i, lane, K, rows), g_lds_addr(dst + A::x_lds(i, 0)));
   }
 }
 
@@ -331,21 +318,14 @@ void gemm_region_mfma(GemmParams p) {
   const int wm = wave & 1, wn = wave >> 1;  // wave's rows [128 wm, +128), cols [64 wn, +64)
 
   // loop-invariant lane offsets of the copies (bytes, from the tile base)
-  const uint32_t lw = (uint32_t)((int64_t)(lane / 16) * p.N * 2 + 16 * ((lane % 16) ^ (4 * ((lane / 16) & 3))));
-  const uint32_t lx = (uint32_t)((int64_t)(lane / 4) * p.K * 2 + 16 * ((lane % 4) ^ ((lane >> 4) & 1)));
+  const uint32_t lw = GemmTileAddr::w_lane_off(lane, p.N);
+  const uint32_t lx = GemmTileAddr::x_lane_off(lane, p.K);
   // LDS operand offsets within a stage, k-step 0: W^T (transposed reads) for
   // the wave's two 32-col blocks, X for its four 32-row blocks
   uint32_t aoff[2];
-  {
-    const int j = lane & 15, q16 = (lane >> 4) & 1;
-    const int row = 8 * g + j / 4;  // + 16 s (+ 4 for the upper half): row % 4 unchanged
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int c = 8 * wn + 4 * nb + 2 * q16 + (j & 3) / 2;
-      aoff[nb] = row * (HN * 2) + ((c ^ (4 * (row & 3))) * 16) + 8 * (j & 1);
-    }
-  }
-  const uint32_t boff = (128 * wm + l32) * (HK * 2) + ((g ^ ((l32 >> 2) & 1)) * 16);
+  for (int nb = 0; nb < 2; ++nb) aoff[nb] = GemmTileAddr::a_read_off(wn, nb, lane);
+  const uint32_t boff = GemmTileAddr::b_read_off(wm, lane);
 
   f32x16_t acc[2][4];
 #pragma unroll
