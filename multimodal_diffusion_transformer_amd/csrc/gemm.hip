@@ -117,6 +117,33 @@ __device__ inline void gemm_store_lds(bf16_t* xs, bf16_t* ws, uint4 (&xr)[4], ui
   }
 }
 
+// Applies the epilogue to 4 consecutive outputs at element offset e and
+// stores them (the residual, if any, is read at the same offset).
+template <bool OUT_BF16, int EPI>
+__device__ __forceinline__ void store4(const GemmParams& p, int64_t e, float (&o)[4]) {
+  if (EPI == EPI_GELU) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) o[t] = gelu_erf(o[t]);
+  } else if (EPI == EPI_ADD) {
+    if (OUT_BF16) {
+      const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.res) + e);
+      o[0] += __uint_as_float(r.x << 16); o[1] += __uint_as_float(r.x & 0xFFFF0000u);
+      o[2] += __uint_as_float(r.y << 16); o[3] += __uint_as_float(r.y & 0xFFFF0000u);
+    } else {
+      const float4 r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.res) + e);
+      o[0] += r.x; o[1] += r.y; o[2] += r.z; o[3] += r.w;
+    }
+  }
+  if (OUT_BF16) {
+    uint2 v;
+    v.x = g_pack_bf16(o[0], o[1]);
+    v.y = g_pack_bf16(o[2], o[3]);
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.y) + e) = v;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + e) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 template <bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(256) void gemm_region_bf16(GemmParams p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -195,28 +222,7 @@ __global__ __launch_bounds__(256) void gemm_region_bf16(GemmParams p) {
         const int64_t n = n0 + 64 * wn + 32 * i + 8 * rr + 4 * g;
         if (n >= p.N) continue;
         float o[4] = {acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1], acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]};
-        const int64_t e = row * p.N + n;  // the store's offset; the residual is read there too
-        if (EPI == EPI_GELU) {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) o[t] = gelu_erf(o[t]);
-        } else if (EPI == EPI_ADD) {
-          if (OUT_BF16) {
-            const uint2 r = *reinterpret_cast<const uint2*>(reinterpret_cast<const bf16_t*>(p.res) + e);
-            o[0] += __uint_as_float(r.x << 16); o[1] += __uint_as_float(r.x & 0xFFFF0000u);
-            o[2] += __uint_as_float(r.y << 16); o[3] += __uint_as_float(r.y & 0xFFFF0000u);
-          } else {
-            const float4 r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.res) + e);
-            o[0] += r.x; o[1] += r.y; o[2] += r.z; o[3] += r.w;
-          }
-        }
-        if (OUT_BF16) {
-          uint2 v;
-          v.x = g_pack_bf16(o[0], o[1]);
-          v.y = g_pack_bf16(o[2], o[3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.y) + e) = v;
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + e) = make_float4(o[0], o[1], o[2], o[3]);
-        }
+        store4<OUT_BF16, EPI>(p, row * p.N + n, o);
       }
   }
 }
@@ -296,7 +302,7 @@ __device__ __forceinline__ void h_issue(const GemmParams& p, const bf16_t* w, in
   }
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_region_mfma(GemmParams p) {
   extern __shared__ __align__(16) unsigned char hsm[];
@@ -392,18 +398,29 @@ void gemm_region_mfma(GemmParams p) {
       for (int rr = 0; rr < 4; ++rr) {
         const int64_t n = n0 + 64 * wn + 32 * nb + 8 * rr + 4 * g;
         if (n >= p.N) continue;
-        if (OUT_BF16) {
-          uint2 v;
-          v.x = g_pack_bf16(acc[nb][mb][4 * rr + 0], acc[nb][mb][4 * rr + 1]);
-          v.y = g_pack_bf16(acc[nb][mb][4 * rr + 2], acc[nb][mb][4 * rr + 3]);
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.y) + row * p.N + n) = v;
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.y) + row * p.N + n) =
-              make_float4(acc[nb][mb][4 * rr + 0], acc[nb][mb][4 * rr + 1], acc[nb][mb][4 * rr + 2],
-                          acc[nb][mb][4 * rr + 3]);
-        }
+        float o[4] = {acc[nb][mb][4 * rr + 0], acc[nb][mb][4 * rr + 1], acc[nb][mb][4 * rr + 2],
+                      acc[nb][mb][4 * rr + 3]};
+        store4<OUT_BF16, EPI>(p, row * p.N + n, o);
       }
   }
+}
+
+template <bool OB>
+static hipError_t launch_dma_gemm(const GemmParams& p, int epi, int64_t blocks, hipStream_t s) {
+  static std::atomic<bool> configured[3] = {{false}, {false}, {false}};
+  const void* fn = epi == EPI_GELU ? (const void*)gemm_region_mfma<OB, EPI_GELU>
+                   : epi == EPI_ADD ? (const void*)gemm_region_mfma<OB, EPI_ADD>
+                                    : (const void*)gemm_region_mfma<OB, EPI_NONE>;
+  if (!configured[epi].load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, H_SMEM_BYTES);
+    if (e != hipSuccess) return e;
+    configured[epi].store(true, std::memory_order_release);
+  }
+  const dim3 grid((unsigned)blocks), block(256);
+  if (epi == EPI_GELU) hipLaunchKernelGGL((gemm_region_mfma<OB, EPI_GELU>), grid, block, H_SMEM_BYTES, s, p);
+  else if (epi == EPI_ADD) hipLaunchKernelGGL((gemm_region_mfma<OB, EPI_ADD>), grid, block, H_SMEM_BYTES, s, p);
+  else hipLaunchKernelGGL((gemm_region_mfma<OB, EPI_NONE>), grid, block, H_SMEM_BYTES, s, p);
+  return hipGetLastError();
 }
 
 #endif  // MOT_GEMM_DMA
@@ -503,25 +520,13 @@ hipError_t region_gemm(const void* x, const void* w_ar, const void* w_dm, void* 
   p.row0[1] = n_ar; p.rows[1] = n_rows - n_ar;
   p.K = K; p.N = N;
 #if defined(MOT_GEMM_DMA) && MOT_GEMM_DMA
-  if (K % HK == 0 && N % 64 == 0 && epi == EPI_NONE) {  // direct-to-LDS MFMA kernel
-    const int ob = out_dt == MOT_BF16 ? 1 : 0;
+  if (K % HK == 0 && N % 64 == 0) {  // direct-to-LDS MFMA kernel
     p.tiles_m[0] = (int)((p.rows[0] + HM - 1) / HM);
     p.tiles_m[1] = (int)((p.rows[1] + HM - 1) / HM);
     p.tiles_n = (int)((N + HN - 1) / HN);
     const int64_t blocks = (int64_t)(p.tiles_m[0] + p.tiles_m[1]) * p.tiles_n;
     if (blocks == 0) return hipSuccess;
-    static std::atomic<bool> configured_dma[2] = {{false}, {false}};
-    const void* fn = ob ? (const void*)gemm_region_mfma<true> : (const void*)gemm_region_mfma<false>;
-    if (!configured_dma[ob].load(std::memory_order_acquire)) {
-      hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, H_SMEM_BYTES);
-      if (e != hipSuccess) return e;
-      configured_dma[ob].store(true, std::memory_order_release);
-    }
-    if (ob)
-      hipLaunchKernelGGL(gemm_region_mfma<true>, dim3((unsigned)blocks), dim3(256), H_SMEM_BYTES, s, p);
-    else
-      hipLaunchKernelGGL(gemm_region_mfma<false>, dim3((unsigned)blocks), dim3(256), H_SMEM_BYTES, s, p);
-    return hipGetLastError();
+    return out_dt == MOT_BF16 ? launch_dma_gemm<true>(p, epi, blocks, s) : launch_dma_gemm<false>(p, epi, blocks, s);
   }
 #endif
   p.tiles_m[0] = (int)((p.rows[0] + GM - 1) / GM);
