@@ -194,8 +194,11 @@ def cpu_baseline(wl, budget_s=15.0):
         oattn.attention(q[n_ar:r1], k, v, n_ar, W.AR_CAUSAL_DM_FULL, n_ar=n_ar)
         dt1 = time.perf_counter() - t1
         one_core = oattn.flops((r1 - n_ar) * n, 1, d) / max(dt1, 1e-9) / 1e12
-    return {"value": flops / max(dt, 1e-9) / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    rate = flops / max(dt, 1e-9) / 1e12
+    full = 4.0 * d * wl.n_heads * attention_pairs(n, n_ar) / 1e12  # the workload's attention, TFLOP
+    return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "single_core_value": one_core,
+            "projected_full_workload_s": round(full / max(rate, 1e-12), 1),
             "sample": "fp64 oracle attention over %d DM query rows x %d keys (%d of %d heads "
                       "started, one head at a time), %.1f s of oracle time on %s, %d BLAS threads; "
                       "single_core_value: one block of %d DM rows on 1 thread, %.2f s"
@@ -215,6 +218,8 @@ def main():
                          "projections, attention, GELU MLP, residuals; needs a workload with an MLP "
                          "width)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the auxiliary long-480p attention figure of the default line")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (10 times), the known-size "
@@ -369,9 +374,57 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_from_profile(wl.name) if args.mode == "step" else None},
     }
+    if args.mode == "step" and wl.name == "t2v480p_bf16" and not args.no_long:
+        del den, fns
+        torch.cuda.empty_cache()
+        try:
+            line["t2v480p_long_attention"] = long_480p_attention(dev)
+        except Exception as e:  # an auxiliary figure: report, do not lose the line
+            line["t2v480p_long_attention"] = {"error": repr(e)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
     print(json.dumps(line), flush=True)
+
+
+def long_480p_attention(dev, reps=3):
+    """The attention launch of the long 480p workload (76,954 tokens: 514
+    AR, 1,560 clean, 74,880 noisy; 24 heads of 128), as the step runs it: Q,
+    K, V strided views of one packed [N, 3, H, D] buffer, Q rotated on load.
+    Inputs are random bf16 already on the device; HIP events on the launch
+    stream time `reps` launches after one warm-up."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from multimodal_diffusion_transformer_amd import _binding as B
+
+    wl = W.BY_NAME["t2v480p_long_bf16"]
+    pos, reg, n_ar = B.mot_build_layout(wl.segments)
+    n, h, d = pos.shape[0], wl.n_heads, wl.head_dim
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.wid)
+    Y = torch.randn((n, 3, h, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    O = torch.empty((n, h, d), dtype=torch.bfloat16, device=dev)
+    P = torch.from_numpy(pos).to(dev)
+    a = B.attn_args(Y[:, 0], Y[:, 1], Y[:, 2], O, mask=B.MOT_AR_CAUSAL_DM_FULL, n_ar=n_ar, q_pos=P,
+                    sections=wl.sections, theta=wl.theta)
+    B.mot_attention_fwd_args(a)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        B.mot_attention_fwd_args(a)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    flops = 4.0 * d * h * attention_pairs(n, n_ar)
+    med = float(np.median(ms))
+    tf = flops / (med * 1e-3) / 1e12
+    del Y, O
+    torch.cuda.empty_cache()
+    return {"tokens": n, "tflop_per_launch": round(flops / 1e12, 3), "ms_median": round(med, 3),
+            "ms_min": round(float(np.min(ms)), 3), "tflops": round(tf, 2),
+            "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
 
 
 def rocprof_summary(d):
