@@ -218,6 +218,9 @@ def main():
                          "projections, attention, GELU MLP, residuals; needs a workload with an MLP "
                          "width)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", type=int, default=1, choices=[1, 2],
+                    help="streaming workload: split each call's keys in two halves over a batch of "
+                         "two launches and merge them through their LSE")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the auxiliary long-480p attention figure of the default line")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -483,7 +486,7 @@ def bench_stream(args, wl):
     def randn(*shape):
         return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
 
-    st = pipeline.StreamState(h, d, n_prefix, ft, slots, wl.sections, wl.theta, device=dev)
+    st = pipeline.StreamState(h, d, n_prefix, ft, slots, wl.sections, wl.theta, device=dev, split=args.split)
     st.fill(randn(nhist, h, d), randn(nhist, h, d), torch.from_numpy(pos[:nhist]).to(dev))
     n_calls = wl.stream_chunks * wl.stream_steps
     qs = [randn(ft, h, d) for _ in range(n_calls)]
@@ -538,7 +541,8 @@ def bench_stream(args, wl):
                                % (wl.name, ft, wl.stream_views, wl.stream_gh, wl.stream_gw, nhist + ft,
                                   n_prefix, slots, wl.stream_chunks, wl.stream_steps),
                    "heads": h, "head_dim": d, "mask": "CHUNK_CAUSAL_KV",
-                   "step": "per call: K/V chunk into the cache + mRoPE(K chunk) + attention (Q on load)"},
+                   "step": "per call: K/V chunk into the cache + mRoPE(K chunk) + attention (Q on load)"
+                           + (" over two key halves in one launch + merge" if args.split == 2 else "")},
         "attention_call_ms": {"median": round(med, 4), "min": round(float(np.min(per_call)), 4)},
         "attention_call_tflops_median": round(call_flops / (med * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL,

@@ -244,6 +244,28 @@ typedef struct {
  * n_heads <= 65535. */
 mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
 
+/* Attention over disjoint key sets merged into attention over their union
+ * (the softmax of the method page's §3 equations over all keys):
+ *     L = log sum_b exp(L_b),   O = sum_b exp(L_b - L) O_b,   LSE = L.
+ * With the batch of mot_attention_fwd over key ranges, this splits one
+ * query tile's keys over several workgroups, for calls whose query tiles
+ * alone leave the chip idle (the streaming chunk).
+ * o_parts: n_parts outputs, part b at o_parts + b * part_stride elements,
+ * each [nq][H][D] with token / head strides p_ts / p_hs; lse_parts: fp32
+ * [n_parts][H][nq], each part's natural-log LSE as mot_attention_fwd writes
+ * it.  o: [nq][H][D] with strides o_ts / o_hs; lse (nullable): fp32 [H][nq]
+ * of the union.  Element type dt (bf16 or fp32) for o_parts and o.  In
+ * fp32: the max of the parts' LSE, their weights exp(L_b - max), the
+ * weighted sum, then division by the weights' sum.  A part whose LSE is
+ * -inf for a row (no key) gets weight 0.  1 <= n_parts <= 16; head_dim 64 or
+ * 128; nq == 0 is a no-op.  One lane per (row, head, 8 dims): nq * H * D/8
+ * <= 2^32 - 256.  INVALID_ARG for null or misaligned pointers, bad strides,
+ * counts or dtype; UNSUPPORTED past the dispatch limit. */
+mot_status mot_attention_merge(const void* o_parts, const float* lse_parts, int32_t n_parts,
+                               int64_t part_stride, int64_t nq, int32_t n_heads, int32_t head_dim,
+                               int64_t p_ts, int64_t p_hs, void* o, int64_t o_ts, int64_t o_hs,
+                               float* lse, int32_t dt, void* stream);
+
 /* Flow-matching Euler update (method page §7.2), in place:
  *     x[e] = x[e] + (sigma_next - sigma) * v[e],   e < n
  * x: device fp32; v: device bf16 or fp32 (v_dt), contiguous.  The step

@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     flow_cfg_euler_step, flow_euler_step, mask_args, mot_layernorm_region, mot_region_linear,
     MOT_EPI_NONE, MOT_EPI_GELU, MOT_EPI_ADD, mot_abi_version, mot_attention_fwd, mot_attention_fwd_args,
     mot_build_layout, mot_mask_materialize, mot_qkv_project, mot_sigma_schedule, mot_status_string,
-    mot_tile_classes_host, mrope_apply, raw_call, mot_attn_args, mot_segment,
+    mot_tile_classes_host, mrope_apply, raw_call, mot_attn_args, mot_segment, mot_attention_merge,
 )

@@ -32,7 +32,7 @@ EXPORTED = [
     "mot_abi_version", "mot_status_string", "mot_build_layout", "mot_qkv_project",
     "mrope_apply", "mot_attention_fwd", "flow_euler_step", "mot_mask_materialize",
     "mot_tile_classes_host", "mot_sigma_schedule", "flow_cfg_euler_step", "mot_region_linear",
-    "mot_layernorm_region",
+    "mot_layernorm_region", "mot_attention_merge",
 ]
 
 
@@ -86,6 +86,9 @@ _lib.mot_region_linear.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, c
 _lib.mot_layernorm_region.restype = ctypes.c_int
 _lib.mot_layernorm_region.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _f32,
                                       ctypes.c_int, ctypes.c_int, _vp]
+_lib.mot_attention_merge.restype = ctypes.c_int
+_lib.mot_attention_merge.argtypes = [_vp, _vp, _i32, _i64, _i64, _i32, _i32, _i64, _i64, _vp, _i64, _i64,
+                                     _vp, ctypes.c_int, _vp]
 _lib.mrope_apply.restype = ctypes.c_int
 _lib.mrope_apply.argtypes = [_vp, ctypes.c_int, _i64, _i32, _i32, _i64, _i64, _vp, _i32, _i32,
                              _i32, _f32, _vp]
@@ -268,6 +271,21 @@ def mot_attention_fwd(q, k, v, o, *, mask, stream=None, **kw):
     a = attn_args(q, k, v, o, mask=mask, **kw)
     st = _lib.mot_attention_fwd(ctypes.byref(a), _stream(stream))
     _check("mot_attention_fwd", st)
+
+
+def mot_attention_merge(o_parts, lse_parts, o, lse=None, stream=None):
+    """Merge per-key-range attention outputs o_parts [B, nq, H, D] (batch
+    stride = part stride) with their LSE [B, H, nq] into o [nq, H, D]."""
+    _need_cuda(o_parts, lse_parts, o, lse)
+    nb, nq, h, d = o_parts.shape
+    if o_parts.stride(3) != 1 or o.stride(2) != 1 or not lse_parts.is_contiguous():
+        raise ValueError("mot_attention_merge: last dims contiguous, LSE parts contiguous")
+    if tuple(lse_parts.shape) != (nb, h, nq) or tuple(o.shape) != (nq, h, d):
+        raise ValueError("mot_attention_merge: shapes differ")
+    st = _lib.mot_attention_merge(_ptr(o_parts), _ptr(lse_parts), nb, o_parts.stride(0), nq, h, d,
+                                  o_parts.stride(1), o_parts.stride(2), _ptr(o), o.stride(0), o.stride(1),
+                                  _ptr(lse), _dtype_code(o), _stream(stream))
+    _check("mot_attention_merge", st)
 
 
 def mot_attention_fwd_args(a, stream=None):

@@ -267,10 +267,16 @@ class BlockStep:
 
 
 class StreamState:
-    """Rolling KV cache for chunk-causal streaming attention."""
+    """Rolling KV cache for chunk-causal streaming attention.
+
+    With split = 2 each call splits its keys in two halves over a batch of
+    two launches (item b reads keys [b nk/2, (b+1) nk/2); the newest chunk
+    sees every key, so each half is plain full attention) and merges the
+    halves' outputs through their LSE: twice the workgroups for the same
+    query tiles."""
 
     def __init__(self, n_heads, head_dim, n_prefix, frame_tokens, slots, sections, theta,
-                 device="cuda"):
+                 device="cuda", split=1):
         self.h, self.d = n_heads, head_dim
         self.n_prefix, self.ft, self.slots = n_prefix, frame_tokens, slots
         self.sections, self.theta = sections, theta
@@ -280,6 +286,13 @@ class StreamState:
         self.V = torch.empty_like(self.K)
         self.pos = torch.empty((nk, 3), dtype=torch.float32, device=device)
         self.q0 = n_prefix + slots * frame_tokens  # the current chunk's rows
+        if split not in (1, 2) or (split == 2 and nk % 2):
+            raise ValueError("split is 1, or 2 with an even key count")
+        self.split = split
+        if split == 2:
+            self.O_parts = torch.empty((2, frame_tokens, n_heads, head_dim), dtype=torch.bfloat16,
+                                       device=device)
+            self.L_parts = torch.empty((2, n_heads, frame_tokens), dtype=torch.float32, device=device)
 
     def fill(self, k_raw, v, pos):
         """Load prefix + history (raw keys, rotated here) into the cache."""
@@ -297,9 +310,22 @@ class StreamState:
         self.V[a:a + self.ft].copy_(v)
         self.pos[a:a + self.ft].copy_(pos)
         B.mrope_apply(self.K[a:a + self.ft], self.pos[a:a + self.ft], self.sections, self.theta)
-        B.mot_attention_fwd(q, self.K, self.V, out, mask=B.MOT_CHUNK_CAUSAL_KV, q0=self.q0,
-                            n_prefix=self.n_prefix, chunk_len=self.ft, q_pos=pos,
-                            sections=self.sections, theta=self.theta, lse=lse)
+        if self.split == 1:
+            B.mot_attention_fwd(q, self.K, self.V, out, mask=B.MOT_CHUNK_CAUSAL_KV, q0=self.q0,
+                                n_prefix=self.n_prefix, chunk_len=self.ft, q_pos=pos,
+                                sections=self.sections, theta=self.theta, lse=lse)
+            return
+        # the chunk is the newest: every key is visible, so each half of the
+        # keys is full attention (every query row a DM row of the AR mask)
+        half = self.nk // 2
+        k2 = torch.as_strided(self.K, (2, half, self.h, self.d),
+                              (half * self.K.stride(0),) + tuple(self.K.stride()), self.K.storage_offset())
+        v2 = torch.as_strided(self.V, (2, half, self.h, self.d),
+                              (half * self.V.stride(0),) + tuple(self.V.stride()), self.V.storage_offset())
+        q2 = q.unsqueeze(0).expand(2, *q.shape)
+        B.mot_attention_fwd(q2, k2, v2, self.O_parts, mask=B.MOT_AR_CAUSAL_DM_FULL, q0=0, n_ar=0,
+                            q_pos=pos, sections=self.sections, theta=self.theta, lse=self.L_parts)
+        B.mot_attention_merge(self.O_parts, self.L_parts, out, lse=lse)
 
     def append(self, chunk_index):
         """Move the current chunk (rotated K, V, positions) into its ring slot."""

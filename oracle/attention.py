@@ -142,6 +142,21 @@ def attention_bruteforce(q, k, v, q0, mode, n_ar=0, n_prefix=0, chunk_len=1,
     return np.array(o), np.array(lse)
 
 
+def merge(o_parts, lse_parts):
+    """Combine attention over disjoint key sets into attention over their
+    union: with L = log sum_b exp(L_b), O = sum_b exp(L_b - L) O_b and the
+    union's LSE is L.  o_parts [B, nq, H, D], lse_parts [B, H, nq]; a part
+    with no keys for a row has L_b = -inf and weight 0."""
+    o = np.asarray(o_parts, dtype=np.float64)
+    l = np.asarray(lse_parts, dtype=np.float64)
+    m = l.max(axis=0)
+    w = np.exp(l - m[None])                    # [B, H, nq]
+    tot = w.sum(axis=0)
+    lse = m + np.log(tot)
+    wt = np.transpose(w / tot[None], (0, 2, 1))[..., None]  # [B, nq, H, 1]
+    return (wt * o).sum(axis=0), lse
+
+
 def flops(pairs: int, n_heads: int, head_dim: int) -> float:
     """Algorithmic FLOPs of masked attention: 2*D for q.k and 2*D for p*v
     per allowed (query, key, head) triple; masked pairs are not counted."""

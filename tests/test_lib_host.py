@@ -308,3 +308,18 @@ def test_projection_and_rope_and_euler_reject_bad_args():
                         None) == mot.MOT_ERR_UNSUPPORTED
     assert mot.raw_call("mot_layernorm_region", None, None, 0, 0, 64, None, None, None, None,
                         f(1e-6), 0, 0, None) == mot.MOT_OK
+    # attention merge: part count, head_dim, strides, alignment, dtype; nq 0 is a no-op
+    for args in [(P, P, 0, 0, 10, 2, 128, 256, 128, P, 256, 128, None, 0),
+                 (P, P, 17, 0, 10, 2, 128, 256, 128, P, 256, 128, None, 0),
+                 (P, P, 2, 0, 10, 2, 96, 256, 128, P, 256, 128, None, 0),
+                 (P, P, 2, 4, 10, 2, 128, 256, 128, P, 256, 128, None, 0),
+                 (P, P, 2, 0, 10, 2, 128, 250, 128, P, 256, 128, None, 0),
+                 (vp(4100), P, 2, 0, 10, 2, 128, 256, 128, P, 256, 128, None, 0),
+                 (P, vp(4098), 2, 0, 10, 2, 128, 256, 128, P, 256, 128, None, 0),
+                 (P, P, 2, 0, 10, 2, 128, 256, 128, P, 256, 128, None, 5),
+                 (None, P, 2, 0, 10, 2, 128, 256, 128, P, 256, 128, None, 0)]:
+        assert mot.raw_call("mot_attention_merge", *args, None) == mot.MOT_ERR_INVALID_ARG, args
+    assert mot.raw_call("mot_attention_merge", None, None, 2, 0, 0, 2, 128, 256, 128, None, 256, 128,
+                        None, 0, None) == mot.MOT_OK
+    assert mot.raw_call("mot_attention_merge", P, P, 2, 0, 1 << 40, 2, 128, 256, 128, P, 256, 128,
+                        None, 0, None) == mot.MOT_ERR_UNSUPPORTED

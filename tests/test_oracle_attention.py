@@ -148,3 +148,32 @@ def test_huge_scores_stay_finite():
     for i in range(3):
         np.testing.assert_allclose(o[i, 0], v[1, 0], rtol=0, atol=1e-15)
         np.testing.assert_allclose(lse[0, i], 1000.0, rtol=0, atol=1e-12)  # 2000 * 1/sqrt(4)
+
+
+def test_merge_of_key_partitions_is_attention_over_all_keys():
+    # softmax attention over a union of key sets from the parts' outputs and
+    # log-sum-exps: the identity a key-split launch relies on
+    rng = np.random.default_rng(71)
+    nq, nk, h, d = 9, 40, 3, 8
+    q, k, v = rng.standard_normal((nq, h, d)), rng.standard_normal((nk, h, d)), rng.standard_normal((nk, h, d))
+    full, lse_full = attention.attention(q, k, v, nk, W.AR_CAUSAL_DM_FULL, n_ar=0)
+    for cuts in ([20], [7, 25], [1], [39]):
+        edges = [0] + cuts + [nk]
+        parts = [attention.attention(q, k[a:b], v[a:b], b - a, W.AR_CAUSAL_DM_FULL, n_ar=0)
+                 for a, b in zip(edges[:-1], edges[1:])]
+        o, lse = attention.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        np.testing.assert_allclose(o, full, atol=1e-13)
+        np.testing.assert_allclose(lse, lse_full, atol=1e-13)
+
+
+def test_merge_single_part_and_empty_part():
+    rng = np.random.default_rng(72)
+    o1, l1 = rng.standard_normal((1, 4, 2, 8)), rng.standard_normal((1, 2, 4))
+    o, l = attention.merge(o1, l1)
+    np.testing.assert_allclose(o, o1[0], atol=1e-15)
+    np.testing.assert_allclose(l, l1[0], atol=1e-15)
+    # a part with no keys (LSE = -inf) has weight 0
+    o2 = np.concatenate([o1, rng.standard_normal((1, 4, 2, 8))])
+    l2 = np.concatenate([l1, np.full((1, 2, 4), -np.inf)])
+    o, l = attention.merge(o2, l2)
+    np.testing.assert_allclose(o, o1[0], atol=1e-15)
