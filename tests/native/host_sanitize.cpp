@@ -277,6 +277,12 @@ static void device_argument_checks() {
   EXPECT(mot_layernorm_region(P16, P16B, (int64_t)1 << 40, 4, 64, (const float*)P16, (const float*)P16,
                               (const float*)P16, (const float*)P16, 1e-6f, MOT_BF16, MOT_BF16, NULL) ==
              MOT_ERR_UNSUPPORTED, "layernorm dispatch too large");
+  EXPECT(mot_attention_merge(P16, (const float*)P16, 0, 0, 10, 2, 128, 256, 128, P16B, 256, 128, NULL,
+                             MOT_BF16, NULL) == MOT_ERR_INVALID_ARG, "merge no parts");
+  EXPECT(mot_attention_merge(P16, (const float*)P16, 2, 4, 10, 2, 128, 256, 128, P16B, 256, 128, NULL,
+                             MOT_BF16, NULL) == MOT_ERR_INVALID_ARG, "merge part stride");
+  EXPECT(mot_attention_merge(P16, (const float*)P16, 2, 0, (int64_t)1 << 40, 2, 128, 256, 128, P16B, 256, 128,
+                             NULL, MOT_BF16, NULL) == MOT_ERR_UNSUPPORTED, "merge dispatch too large");
   a = args(10, 5, 0, 0, 3, 0, 0);
   EXPECT(mot_mask_materialize(&a, (uint8_t*)P16, 128, 64, NULL, NULL) == MOT_ERR_INVALID_ARG,
          "mask invalid args");
