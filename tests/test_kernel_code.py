@@ -107,3 +107,38 @@ def test_each_key_step_is_branch_free_and_spill_free(tmp_path):
             assert not spill, (name, spill[:5])
         checked += 1
     assert checked == 4
+
+
+def _all_kernel_metadata(tmp_path):
+    out = {}
+    for co in _code_objects(tmp_path):
+        notes = subprocess.run([os.path.join(LLVM, "llvm-readelf"), "--notes", str(co)],
+                               capture_output=True, text=True, check=True).stdout
+        for block in re.split(r"\n\s*- \.", notes):
+            m = re.search(r"\.name:\s+(\S+)", block)
+            if m:
+                out[m.group(1)] = dict(re.findall(r"\.(\w+):\s+(\S+)", "." + block))
+    return out
+
+
+# the bandwidth-bound kernels and the region GEMM: no scratch spills; the
+# HBM-bound kernels keep at least 4 waves per SIMD (<= 128 VGPRs), except the
+# LayerNorm instance for rows past 4,096 columns, which holds 16 chunks of
+# 16 bytes per lane in registers (2 waves per SIMD, 16 loads in flight each)
+NO_SPILL = ("layernorm_kernel", "attn_merge_kernel", "euler_kernel", "mrope_kernel", "gemm_region_bf16")
+HBM_BOUND = ("layernorm_kernel", "attn_merge_kernel", "euler_kernel", "mrope_kernel")
+
+
+def test_other_kernels_spill_free(tmp_path):
+    md = _all_kernel_metadata(tmp_path)
+    seen = set()
+    for name, kv in md.items():
+        hit = [k for k in NO_SPILL if k in name]
+        if not hit:
+            continue
+        seen |= set(hit)
+        assert int(kv.get("private_segment_fixed_size", "0")) == 0, (name, kv.get("private_segment_fixed_size"))
+        if any(k in name for k in HBM_BOUND):
+            limit = 256 if "layernorm_kernelILi16E" in name else 128
+            assert int(kv["vgpr_count"]) <= limit, (name, kv["vgpr_count"])
+    assert seen == set(NO_SPILL), sorted(seen)
