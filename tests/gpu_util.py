@@ -51,15 +51,22 @@ def bf16_spacing(v):
     return np.where(a > 0, np.exp2(e - 7), 0.0)
 
 
-def assert_parity_stored(got, want, what=""):
+def assert_parity_stored(got, want, what="", spacings=1):
     """The bf16 contract for a tensor stored in bf16 whose values may be
-    large: relative L2 <= 5e-3, and per element |got - want| <=
-    max(2e-2, one bf16 spacing of want).  Storing a value in bf16 moves it
-    by up to half a spacing, which passes 2e-2 once |value| >= 8 (and two
-    stored results may sit a spacing apart from |value| >= 4)."""
+    large: relative L2 <= 5e-3, and per element |got - want| <= max(2e-2,
+    `spacings` bf16 spacings at the larger of |got| and |want|).  Storing a
+    value in bf16 moves it by up to half a spacing, which passes 2e-2 once
+    |value| >= 8, and two stored results may sit a spacing apart from
+    |value| >= 4; where they straddle a power of two, that spacing is the
+    upper binade's.  A stored value that adds to an earlier stored value
+    compared end to end (H2 = round(H1 + delta) against the oracle's own H1)
+    carries that one's spacing too: spacings=2."""
     ma, rl = errors(got, want)
-    d = np.abs(np.asarray(got, np.float64) - np.asarray(want, np.float64))
-    worst = float((d / np.maximum(BF16_MAX_ABS, bf16_spacing(want))).max()) if d.size else 0.0
+    g = np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    d = np.abs(g - w)
+    allow = np.maximum(BF16_MAX_ABS, spacings * bf16_spacing(np.maximum(np.abs(g), np.abs(w))))
+    worst = float((d / allow).max()) if d.size else 0.0
     say("  parity %-28s max_abs=%.3e rel_l2=%.3e worst/allowance=%.2f (stored bf16)" % (what, ma, rl, worst))
     assert rl <= BF16_REL_L2 and worst <= 1.0, (what, ma, rl, worst)
     return ma, rl
