@@ -438,7 +438,8 @@ def test_region_linear_bf16_epilogues(E, out_dt, epi, in_place):
 
 
 @pytest.mark.parametrize("epi", [0, 1, 2])
-@pytest.mark.parametrize("case", [(70, 30, 40, 50), (33, 0, 16, 17), (16, 16, 64, 32)],
+@pytest.mark.parametrize("case", [(70, 30, 40, 50), (33, 0, 16, 17), (16, 16, 64, 32), (20, 20, 24, 8),
+                                  (20, 0, 24, 8), (37, 19, 16, 16)],
                          ids=lambda c: "n%d_ar%d_K%d_N%d" % c)
 def test_region_linear_fp32(E, case, epi):
     E.config(False, True)
@@ -675,6 +676,9 @@ PLANTED = [
     ("GEMM epilogue residual row", [("gemm.hip", "store4<OUT_BF16, EPI>(p, row * p.N + n, o);\n      }\n  }\n}\n\n//",
                                      "store4<OUT_BF16, EPI>(p, (row ^ 1) * p.N + n, o);\n      }\n  }\n}\n\n//")],
      "gemm"),
+    ("fp32 GEMM reads the absent room's weights past the last row",
+     [("gemm.hip", "const int64_t rhi = rlo + FT < M ? rlo + FT : M;", "const int64_t rhi = rlo + FT;")],
+     "gemm_f32_null"),
 ]
 
 
@@ -688,6 +692,11 @@ def test_planted_mistake_is_caught(tmp_path, what, patches, kind):
             try:
                 if kind == "gemm":
                     _check_gemm(Ep, (300, 130, 128, 192), BF16, 0, False)
+                elif kind == "gemm_f32_null":
+                    x, wa, _ = _gemm_inputs((20, 20, 24, 8), "fp32")
+                    Y = Ep.empty((20, 8), np.float32)
+                    region_linear(Ep, Ep.array(x.f32), Ep.array(wa.f32), None, Y, 20, FP32, FP32)
+                    assert_parity(Y, oproj.project(x.f32, wa.f32, wa.f32, 20), "fp32", what)
                 else:
                     nq, h, hk, d = 300, 8, 2, 128
                     q, k, v = _qkv(7, nq, nq, h, hk, d, "bf16")
