@@ -8,6 +8,11 @@ BF16_MAX_ABS = 2e-2   # bf16 in / fp32 accumulate vs the fp64 oracle
 BF16_REL_L2 = 5e-3
 F32_MAX_ABS = 1e-4    # fp32 paths (tiny workload): the same contract holds;
 F32_REL_L2 = 1e-5     # these tighter bounds document the fp32 arithmetic
+# The bf16 attention kernel's LSE: its row sum adds the bf16-rounded P that
+# the PV product uses, each within a relative 2^-8 (the unit roundoff of an
+# 8-bit significand), so the sum and the LSE are off by at most
+# ln(1 + 2^-8) = 3.9e-3, plus the fp32 error of the scores (~1e-4).
+BF16_LSE_ATOL = 4e-3
 
 
 def device():

@@ -1,0 +1,215 @@
+"""Randomised parity of the kernels on the CPU SIMT emulator (see
+tests/test_emu_kernels.py): hypothesis draws valid problems (shapes, ragged
+sizes, masks, query offsets, grouped heads, batches, padded strides, score
+scales, scheduling modes) and each is compared with the oracle at the GPU
+tests' tolerances.  Derandomised, so every run draws the same examples.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+import pytest
+
+hyp = pytest.importorskip("hypothesis")
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+import workloads as W  # noqa: E402
+from oracle import attention as oattn  # noqa: E402
+from oracle import block as oblock  # noqa: E402
+from oracle import denoiser as odenoiser  # noqa: E402
+from oracle import mrope as omrope  # noqa: E402
+from oracle import projection as oproj  # noqa: E402
+from tests import emu_lib  # noqa: E402
+from tests.gpu_util import BF16_LSE_ATOL, assert_parity, assert_parity_stored  # noqa: E402
+from tests.test_emu_kernels import BF16, FP32, _el, attention, bits_of, region_linear, val  # noqa: E402
+
+pytestmark = pytest.mark.skipif(not os.path.exists(emu_lib.CXX), reason="host clang++ missing")
+AR, CH = W.AR_CAUSAL_DM_FULL, W.CHUNK_CAUSAL_KV
+SETTINGS = dict(deadline=None, derandomize=True, suppress_health_check=list(HealthCheck), database=None)
+# MOT_FUZZ_SCALE=k draws k times as many examples (a longer run by hand)
+SCALE = int(os.environ.get("MOT_FUZZ_SCALE", "1"))
+
+
+@pytest.fixture(scope="module")
+def E(tmp_path_factory):
+    pytest.importorskip("multimodal_diffusion_transformer_amd._binding")
+    e = emu_lib.Emu(emu_lib.build(str(tmp_path_factory.mktemp("emu_fuzz"))))
+    yield e
+    e.free_all()
+
+
+@st.composite
+def attn_problem(draw):
+    d = draw(st.sampled_from([64, 128]))
+    hk = draw(st.integers(1, 4))
+    h = hk * draw(st.integers(1, 4))
+    mask = draw(st.sampled_from([AR, CH]))
+    nq = draw(st.integers(1, 260))
+    if mask == AR:
+        q0 = draw(st.integers(0, 150))
+        nk = q0 + nq + draw(st.integers(0, 90))
+        n_ar = draw(st.integers(0, nk))
+        n_prefix, cl = 0, 0
+    else:
+        n_prefix = draw(st.integers(0, 130))
+        q0 = n_prefix + draw(st.integers(0, 70))
+        cl = draw(st.integers(1, 160))
+        nk = draw(st.integers(max(n_prefix, 1), q0 + nq + 40))
+        n_ar = 0
+    return dict(d=d, h=h, hk=hk, mask=mask, nq=nq, nk=nk, q0=q0, n_ar=n_ar, n_prefix=n_prefix, cl=cl,
+                batch=draw(st.integers(1, 2)), pad=draw(st.integers(0, 2)),
+                std=draw(st.sampled_from([0.5, 1.0, 2.0])), rope=draw(st.booleans()),
+                mode=draw(st.sampled_from([(False, False), (True, True), (True, False)])),
+                seed=draw(st.integers(0, 10 ** 6)))
+
+
+@settings(max_examples=40 * SCALE, **SETTINGS)
+@given(pr=attn_problem())
+def test_attention_bf16_random_problems(E, pr):
+    d, h, hk, nq, nk, B, pad = pr["d"], pr["h"], pr["hk"], pr["nq"], pr["nk"], pr["batch"], pr["pad"]
+    E.config(*pr["mode"])
+    r = np.random.default_rng(pr["seed"])
+    try:
+        # padded head dimension: every view has a row stride larger than its heads
+        Qb = E.empty((B, nq, h + pad, d), np.uint16)
+        Kb = E.empty((B, nk, hk + pad, d), np.uint16)
+        Vb = E.empty((B, nk, hk + pad, d), np.uint16)
+        Ob = E.empty((B, nq, h + pad, d), np.uint16)
+        L = E.empty((B, h, nq), np.float32)
+        q = bits_of(r.standard_normal((B, nq, h, d)) * pr["std"])
+        k = bits_of(r.standard_normal((B, nk, hk, d)) * pr["std"])
+        v = bits_of(r.standard_normal((B, nk, hk, d)))
+        Qb[:, :, :h], Kb[:, :, :hk], Vb[:, :, :hk] = q, k, v
+        kw = dict(mode=pr["mask"], q0=pr["q0"], n_ar=pr["n_ar"], n_prefix=pr["n_prefix"], chunk_len=pr["cl"])
+        pos, secs = None, (d // 8, 3 * d // 16, 3 * d // 16)
+        if pr["rope"]:
+            pos = E.array(np.floor(r.uniform(0, 2e4, (nq, 3))).astype(np.float32))
+            kw.update(q_pos=pos, sections=secs, theta=1e4)
+        views = [t[:, :, :n] for t, n in ((Qb, h), (Kb, hk), (Vb, hk), (Ob, h))]
+        if B == 1:
+            views = [t[0] for t in views]
+            attention(E, *views, lse=L[0], **kw)
+        else:
+            attention(E, *views, lse=L, **kw)
+        for b in range(B):
+            qf = val(q[b])
+            if pr["rope"]:
+                # the kernel stores the rotated Q in bf16 (its MFMA operand)
+                qf = odenoiser.round_bf16(omrope.apply(qf, np.asarray(pos), secs, 1e4))
+            want, lse = oattn.attention(qf, val(k[b]), val(v[b]), pr["q0"], pr["mask"], pr["n_ar"],
+                                        pr["n_prefix"], max(pr["cl"], 1))
+            assert_parity(val(Ob[b, :, :h]), want, "bf16", "item %d" % b)
+            np.testing.assert_allclose(L[b], lse, atol=BF16_LSE_ATOL, rtol=0)
+            assert (Ob[b, :, h:] == 0).all()  # pad heads untouched
+    finally:
+        E.free_all()
+
+
+@settings(max_examples=15 * SCALE, **SETTINGS)
+@given(d=st.sampled_from([64, 128]), hk=st.integers(1, 3), g=st.integers(1, 3), nq=st.integers(1, 120),
+       extra=st.integers(0, 60), n_ar_frac=st.floats(0, 1), seed=st.integers(0, 10 ** 6))
+def test_attention_fp32_random_problems(E, d, hk, g, nq, extra, n_ar_frac, seed):
+    E.config(False, True)
+    h, nk = hk * g, nq + extra
+    n_ar = int(n_ar_frac * nk)
+    r = np.random.default_rng(seed)
+    try:
+        q = r.standard_normal((nq, h, d)).astype(np.float32)
+        k = r.standard_normal((nk, hk, d)).astype(np.float32)
+        v = r.standard_normal((nk, hk, d)).astype(np.float32)
+        O, L = E.empty((nq, h, d), np.float32), E.empty((h, nq), np.float32)
+        attention(E, E.array(q), E.array(k), E.array(v), O, mode=AR, q0=extra, n_ar=n_ar, lse=L)
+        want, lse = oattn.attention(q, k, v, extra, AR, n_ar)
+        assert_parity(O, want, "fp32", "fp32 attention")
+        np.testing.assert_allclose(L, lse, atol=1e-4, rtol=0)
+    finally:
+        E.free_all()
+
+
+@settings(max_examples=25 * SCALE, **SETTINGS)
+@given(n=st.integers(1, 400), ar_frac=st.floats(0, 1), kb=st.integers(1, 5), nb=st.integers(1, 7),
+       out_dt=st.sampled_from([BF16, FP32]), epi=st.sampled_from([0, 1, 2]),
+       mode=st.sampled_from([(False, False), (True, True)]), seed=st.integers(0, 10 ** 6))
+def test_region_linear_bf16_random_problems(E, n, ar_frac, kb, nb, out_dt, epi, mode, seed):
+    E.config(*mode)
+    K, N = 64 * kb, 64 * nb
+    n_ar = int(ar_frac * n)
+    r = np.random.default_rng(seed)
+    try:
+        x = bits_of(r.standard_normal((n, K)))
+        wa = bits_of(r.standard_normal((K, N)) / math.sqrt(K))
+        wd = bits_of(r.standard_normal((K, N)) / math.sqrt(K))
+        want = oproj.project(val(x), val(wa), val(wd), n_ar)
+        R = None
+        Y = E.empty((n, N), np.uint16 if out_dt == BF16 else np.float32)
+        if epi == 1:
+            want = oblock.gelu(want)
+        elif epi == 2:
+            res = r.standard_normal((n, N)) * 3
+            res = bits_of(res) if out_dt == BF16 else res.astype(np.float32)
+            Y[...] = res
+            R = Y
+            want = want + (val(res) if out_dt == BF16 else res)
+        region_linear(E, E.array(x), E.array(wa) if n_ar > 0 else None, E.array(wd) if n_ar < n else None,
+                      Y, n_ar, BF16, out_dt, epi, R)
+        got = val(Y) if out_dt == BF16 else Y
+        if out_dt == BF16:
+            assert_parity_stored(got, want, "gemm")
+        else:
+            assert_parity(got, want, "bf16", "gemm")
+    finally:
+        E.free_all()
+
+
+@settings(max_examples=20 * SCALE, **SETTINGS)
+@given(hidden8=st.integers(1, 1024), n=st.integers(1, 12), ar_frac=st.floats(0, 1),
+       in_bf16=st.booleans(), out_bf16=st.booleans(), scale=st.sampled_from([0.01, 1.0, 100.0]),
+       seed=st.integers(0, 10 ** 6))
+def test_layernorm_random_problems(E, hidden8, n, ar_frac, in_bf16, out_bf16, scale, seed):
+    E.config(False, False)
+    hidden, n_ar = 8 * hidden8, int(ar_frac * n)
+    r = np.random.default_rng(seed)
+    try:
+        x = (r.standard_normal((n, hidden)) * scale + r.standard_normal((n, 1)) * scale).astype(np.float32)
+        x = val(bits_of(x)) if in_bf16 else x
+        g = [(1 + 0.1 * r.standard_normal(hidden)).astype(np.float32) for _ in range(2)]
+        b = [(0.1 * r.standard_normal(hidden)).astype(np.float32) for _ in range(2)]
+        X = E.array(bits_of(x) if in_bf16 else x)
+        Y = E.empty((n, hidden), np.uint16 if out_bf16 else np.float32)
+        ptrs = [emu_lib.ptr(E.array(t)) for t in (g[0], b[0], g[1], b[1])]
+        st_ = E.call("mot_layernorm_region", emu_lib.ptr(X), emu_lib.ptr(Y), n, n_ar, hidden, *ptrs,
+                     ctypes.c_float(1e-6), BF16 if in_bf16 else FP32, BF16 if out_bf16 else FP32, None)
+        assert st_ == 0
+        want = oblock.region_layer_norm(x, (g[0], b[0]), (g[1], b[1]), n_ar, 1e-6)
+        assert_parity(val(Y) if out_bf16 else Y, want, "bf16" if out_bf16 else "fp32", "layernorm")
+    finally:
+        E.free_all()
+
+
+@settings(max_examples=20 * SCALE, **SETTINGS)
+@given(parts=st.integers(1, 16), nq=st.integers(1, 60), h=st.integers(1, 5), d=st.sampled_from([64, 128]),
+       bf16=st.booleans(), empty_frac=st.floats(0, 0.5), seed=st.integers(0, 10 ** 6))
+def test_merge_random_problems(E, parts, nq, h, d, bf16, empty_frac, seed):
+    E.config(False, False)
+    r = np.random.default_rng(seed)
+    try:
+        o = r.standard_normal((parts, nq, h, d)).astype(np.float32)
+        o = val(bits_of(o)) if bf16 else o
+        lse = (r.standard_normal((parts, h, nq)) * 4).astype(np.float32)
+        # parts with no key for a row; part 0 always has one
+        lse[1:][r.random((parts - 1, h, nq)) < empty_frac] = -np.inf
+        Op = E.array(bits_of(o) if bf16 else o)
+        Lp = E.array(lse)
+        O = E.empty((nq, h, d), np.uint16 if bf16 else np.float32)
+        L = E.empty((h, nq), np.float32)
+        el = _el(Op)
+        st_ = E.call("mot_attention_merge", emu_lib.ptr(Op), emu_lib.ptr(Lp), parts, el[0], nq, h, d, el[1],
+                     el[2], emu_lib.ptr(O), h * d, d, emu_lib.ptr(L), BF16 if bf16 else FP32, None)
+        assert st_ == 0
+        want, wl = oattn.merge(o, lse)
+        assert_parity(val(O) if bf16 else O, want, "bf16" if bf16 else "fp32", "merge")
+        np.testing.assert_allclose(L, wl, atol=1e-5, rtol=1e-6)
+    finally:
+        E.free_all()

@@ -34,7 +34,7 @@ from oracle import layout as olayout
 from oracle import mrope as omrope
 from oracle import projection as oproj
 from tests import emu_lib
-from tests.gpu_util import assert_parity, assert_parity_stored, errors
+from tests.gpu_util import BF16_LSE_ATOL, assert_parity, assert_parity_stored, errors
 
 pytestmark = pytest.mark.skipif(not os.path.exists(emu_lib.CXX), reason="host clang++ missing")
 # the C ABI's argument structure and types, as the product binding declares them
@@ -150,7 +150,7 @@ def test_attention_bf16(E, case, mode):
     attention(E, Q, K, V, O, mode=mask, q0=q0, n_ar=n_ar, n_prefix=n_prefix, chunk_len=cl, lse=L)
     want, lse = oattn.attention(q.f32, k.f32, v.f32, q0, mask, n_ar, n_prefix, max(cl, 1))
     assert_parity(val(O), want, "bf16", name)
-    np.testing.assert_allclose(L, lse, atol=2e-3, rtol=0)
+    np.testing.assert_allclose(L, lse, atol=BF16_LSE_ATOL, rtol=0)
 
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
@@ -191,7 +191,7 @@ def test_attention_bf16_batched_heads_and_strides(E, mode, d):
     for b, (q, k, v) in enumerate(ins):
         want, lse = oattn.attention(q.f32, k.f32, v.f32, 0, AR, n_ar)
         assert_parity(val(O[b]), want, "bf16", "batch item %d" % b)
-        np.testing.assert_allclose(L[b], lse, atol=2e-3, rtol=0)
+        np.testing.assert_allclose(L[b], lse, atol=BF16_LSE_ATOL, rtol=0)
 
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
@@ -217,7 +217,7 @@ def test_attention_key_split_and_merge(E, mode):
     assert st_ == 0
     want, lse = oattn.attention(q.f32, k.f32, v.f32, 0, AR, n_ar=0)
     assert_parity(val(O), want, "bf16", "split + merge")
-    np.testing.assert_allclose(L, lse, atol=2e-3, rtol=0)
+    np.testing.assert_allclose(L, lse, atol=BF16_LSE_ATOL, rtol=0)
 
 
 @pytest.mark.parametrize("d", [128, 64])
@@ -267,7 +267,7 @@ def test_attention_large_scores_move_the_reference(E, kind, hk):
     for b, (qf, kf, vf) in enumerate(ins):
         want, lse = oattn.attention(qf, kf, vf, 0, AR, n_ar=n_ar)
         assert_parity(val(O[b]), want, "bf16", "large scores %s item %d" % (kind, b))
-        np.testing.assert_allclose(L[b], lse, atol=2.5e-3, rtol=1e-5)
+        np.testing.assert_allclose(L[b], lse, atol=BF16_LSE_ATOL, rtol=0)
 
 
 def test_attention_bf16_edge_properties(E):
