@@ -80,3 +80,21 @@ def assert_parity_stored(got, want, what="", spacings=1):
 def to_np(t):
     from workloads import to_numpy_f32
     return to_numpy_f32(t)
+
+
+def stream_workload(size):
+    """The streaming workload ("stream_chunk_bf16"), or ("mini") the same
+    structure reduced to 8-token frames of 2 heads of 64 with an 8-token
+    text prefix and 11 chunks, which still wrap the 8-slot ring."""
+    import dataclasses
+
+    import workloads as W
+    full = W.BY_NAME["stream_chunk_bf16"]
+    if size == "stream_chunk_bf16":
+        return full
+    assert size == "mini", size
+    return dataclasses.replace(
+        full, name="stream_mini_bf16", n_heads=2, head_dim=64, hidden=128, sections=(8, 12, 12),
+        segments=(W.text(6), *W.eos_bog(), W.video(W.DM_CLEAN, 8, 1, 2, 4, frame0=0),
+                  W.video(W.DM_NOISY, 1, 1, 2, 4, frame0=8)),
+        stream_views=1, stream_gh=2, stream_gw=4, stream_chunks=11, stream_text=6)

@@ -9,7 +9,7 @@ import workloads as W
 from oracle import attention as oattn
 from oracle import layout as olayout
 from oracle import streaming as ostream
-from tests.gpu_util import BF16_LSE_ATOL, assert_parity, device, say, to_np
+from tests.gpu_util import BF16_LSE_ATOL, assert_parity, device, say, stream_workload, to_np
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -64,12 +64,14 @@ def test_key_split_launch_equals_attention_over_all_keys():
     np.testing.assert_allclose(to_np(L), lse, atol=BF16_LSE_ATOL, rtol=0)
 
 
-def test_streaming_rollout_with_split_keys():
+@pytest.mark.parametrize("size", ["stream_chunk_bf16", "mini"])
+def test_streaming_rollout_with_split_keys(size):
     """The streaming workload with each call's keys split in two and merged:
-    two chunks x 4 steps against the oracle's rolling cache."""
+    two chunks x 4 steps against the oracle's rolling cache (at the reduced
+    size: every chunk, through the ring wrap)."""
     dev = device()
     from multimodal_diffusion_transformer_amd import pipeline as P
-    wl = W.BY_NAME["stream_chunk_bf16"]
+    wl = stream_workload(size)
     h, d = wl.n_heads, wl.head_dim
     ft = wl.stream_views * wl.stream_gh * wl.stream_gw
     slots = wl.stream_history_frames
@@ -86,7 +88,7 @@ def test_streaming_rollout_with_split_keys():
     chunk_pos = pos[n_prefix + slots * ft:].copy()
     O = torch.empty((ft, h, d), dtype=torch.bfloat16, device=dev)
     rng = np.random.default_rng(62)
-    for c in range(2):
+    for c in range(2 if size == "stream_chunk_bf16" else wl.stream_chunks):
         cp = chunk_pos.copy()
         cp[:, 0] = np.float32(t0 + slots + c)
         for s in range(wl.stream_steps):
@@ -95,8 +97,8 @@ def test_streaming_rollout_with_split_keys():
             v = W.make(3, 62, (ft, h, d), "bf16", 1.0, c, s)
             st.attend(W.to_torch(q, dev), W.to_torch(k, dev), W.to_torch(v, dev), torch.from_numpy(cp).to(dev), O)
             torch.cuda.synchronize()
-            rows = sorted(set(rng.choice(ft, 16, replace=False).tolist()) | {0, ft - 1})
-            heads = [0, 12, 23]
+            rows = sorted(set(rng.choice(ft, min(16, ft), replace=False).tolist()) | {0, ft - 1})
+            heads = sorted({0, h // 2, h - 1})
             want, kr = oc.attend(q.f32, k.f32, v.f32, cp, rows=rows, heads=heads)
             say("split stream chunk %d step %d" % (c, s))
             assert_parity(to_np(O)[rows][:, heads], want, "bf16", "split stream c%d s%d" % (c, s))
