@@ -129,6 +129,8 @@ class Emu:
         self._bufs = []
 
     def config(self, dma_late=False, reverse_waves=False, threads=8):
+        """reverse_waves: False / True, or 2 for a seeded random wave order in
+        every phase between barriers."""
         self.lib.emu_config(int(dma_late), int(reverse_waves), int(threads))
 
     def stat(self, i):

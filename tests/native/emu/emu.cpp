@@ -11,9 +11,10 @@
 //    different ones, or a barrier while others wait at a wave operation,
 //    are reported: that is divergence the kernels must not have);
 //  * a barrier releases once every work-item of the workgroup still running
-//    has reached it.  Between barriers each wave runs alone, in wave order
-//    or in reverse (a setting), so a missing barrier before reading another
-//    wave's LDS data shows up as a wrong result in one of the two orders.
+//    has reached it.  Between barriers each wave runs alone, in wave order,
+//    in reverse, or in a seeded random order per phase (a setting), so a
+//    missing barrier before reading another wave's LDS data shows up as a
+//    wrong result in some order.
 //  * LDS starts filled with 0xFF bytes (NaN in bf16 and fp32) and ends at a
 //    guard page; LDS-DMA copies either land at once ("early") or are held
 //    back until the issuing wave's vmcnt wait, with their destination set
@@ -46,6 +47,7 @@
 #include <mutex>
 #include <string>
 #include <thread>
+#include <utility>
 #include <vector>
 
 #include <sys/mman.h>
@@ -455,8 +457,21 @@ void run_workgroup(Worker* w, uint64_t flat) {
   }
   for (int i = 0; i < nw; ++i) w->pending[i].clear();
   if (w->lds_size) memset(w->lds, 0xFF, w->lds_size);
+  // wave order between barriers: in order, reversed, or a fresh seeded
+  // permutation for every phase (reverse = 2)
+  int order[MAX_ITEMS / 64];
+  uint64_t rs = 0x9E3779B97F4A7C15ull ^ (flat * 0xBF58476D1CE4E5B9ull);
   for (;;) {
-    for (int k = 0; k < nw; ++k) run_wave(w, g_cfg.reverse ? nw - 1 - k : k);
+    for (int k = 0; k < nw; ++k) order[k] = g_cfg.reverse == 1 ? nw - 1 - k : k;
+    if (g_cfg.reverse == 2)
+      for (int k = nw - 1; k > 0; --k) {
+        rs ^= rs << 13;
+        rs ^= rs >> 7;
+        rs ^= rs << 17;
+        const int j = (int)(rs % (uint64_t)(k + 1));
+        std::swap(order[k], order[j]);
+      }
+    for (int k = 0; k < nw; ++k) run_wave(w, order[k]);
     bool any = false;
     for (int t = 0; t < n; ++t)
       if (w->lanes[t].state == AT_BAR) {

@@ -61,7 +61,7 @@ def attn_problem(draw):
     return dict(d=d, h=h, hk=hk, mask=mask, nq=nq, nk=nk, q0=q0, n_ar=n_ar, n_prefix=n_prefix, cl=cl,
                 batch=draw(st.integers(1, 2)), pad=draw(st.integers(0, 2)),
                 std=draw(st.sampled_from([0.5, 1.0, 2.0])), rope=draw(st.booleans()),
-                mode=draw(st.sampled_from([(False, False), (True, True), (True, False)])),
+                mode=draw(st.sampled_from([(False, False), (True, True), (True, False), (True, 2)])),
                 seed=draw(st.integers(0, 10 ** 6)))
 
 
@@ -131,7 +131,7 @@ def test_attention_fp32_random_problems(E, d, hk, g, nq, extra, n_ar_frac, seed)
 @settings(max_examples=25 * SCALE, **SETTINGS)
 @given(n=st.integers(1, 400), ar_frac=st.floats(0, 1), kb=st.integers(1, 5), nb=st.integers(1, 7),
        out_dt=st.sampled_from([BF16, FP32]), epi=st.sampled_from([0, 1, 2]),
-       mode=st.sampled_from([(False, False), (True, True)]), seed=st.integers(0, 10 ** 6))
+       mode=st.sampled_from([(False, False), (True, True), (True, 2)]), seed=st.integers(0, 10 ** 6))
 def test_region_linear_bf16_random_problems(E, n, ar_frac, kb, nb, out_dt, epi, mode, seed):
     E.config(*mode)
     K, N = 64 * kb, 64 * nb
