@@ -1,8 +1,9 @@
 """Randomised parity of the kernels on the CPU SIMT emulator (see
 tests/test_emu_kernels.py): hypothesis draws valid problems (shapes, ragged
-sizes, masks, query offsets, grouped heads, batches, padded strides, score
-scales, scheduling modes) and each is compared with the oracle at the GPU
-tests' tolerances.  Derandomised, so every run draws the same examples.
+sizes, masks, query offsets, grouped heads, batches, padded strides, input
+and softmax scales, mRoPE sections and positions, guidance weights and
+noise levels, scheduling modes) and each is compared with the oracle at the
+GPU tests' tolerances.  Derandomised, so every run draws the same examples.
 """
 import ctypes
 import math
@@ -18,6 +19,8 @@ from hypothesis import strategies as st  # noqa: E402
 import workloads as W  # noqa: E402
 from oracle import attention as oattn  # noqa: E402
 from oracle import block as oblock  # noqa: E402
+from oracle import cfg as ocfg  # noqa: E402
+from oracle import euler as oeuler  # noqa: E402
 from oracle import denoiser as odenoiser  # noqa: E402
 from oracle import mrope as omrope  # noqa: E402
 from oracle import projection as oproj  # noqa: E402
@@ -61,6 +64,7 @@ def attn_problem(draw):
     return dict(d=d, h=h, hk=hk, mask=mask, nq=nq, nk=nk, q0=q0, n_ar=n_ar, n_prefix=n_prefix, cl=cl,
                 batch=draw(st.integers(1, 2)), pad=draw(st.integers(0, 2)),
                 std=draw(st.sampled_from([0.5, 1.0, 2.0])), rope=draw(st.booleans()),
+                scale=draw(st.sampled_from([0.0, 0.0, 0.04, 0.3])),
                 mode=draw(st.sampled_from([(False, False), (True, True), (True, False), (True, 2)])),
                 seed=draw(st.integers(0, 10 ** 6)))
 
@@ -82,7 +86,8 @@ def test_attention_bf16_random_problems(E, pr):
         k = bits_of(r.standard_normal((B, nk, hk, d)) * pr["std"])
         v = bits_of(r.standard_normal((B, nk, hk, d)))
         Qb[:, :, :h], Kb[:, :, :hk], Vb[:, :, :hk] = q, k, v
-        kw = dict(mode=pr["mask"], q0=pr["q0"], n_ar=pr["n_ar"], n_prefix=pr["n_prefix"], chunk_len=pr["cl"])
+        kw = dict(mode=pr["mask"], q0=pr["q0"], n_ar=pr["n_ar"], n_prefix=pr["n_prefix"], chunk_len=pr["cl"],
+                  scale=pr["scale"])
         pos, secs = None, (d // 8, 3 * d // 16, 3 * d // 16)
         if pr["rope"]:
             pos = E.array(np.floor(r.uniform(0, 2e4, (nq, 3))).astype(np.float32))
@@ -99,7 +104,8 @@ def test_attention_bf16_random_problems(E, pr):
                 # the kernel stores the rotated Q in bf16 (its MFMA operand)
                 qf = odenoiser.round_bf16(omrope.apply(qf, np.asarray(pos), secs, 1e4))
             want, lse = oattn.attention(qf, val(k[b]), val(v[b]), pr["q0"], pr["mask"], pr["n_ar"],
-                                        pr["n_prefix"], max(pr["cl"], 1))
+                                        pr["n_prefix"], max(pr["cl"], 1),
+                                        scale=float(np.float32(pr["scale"])) if pr["scale"] else None)
             assert_parity(val(Ob[b, :, :h]), want, "bf16", "item %d" % b)
             np.testing.assert_allclose(L[b], lse, atol=BF16_LSE_ATOL, rtol=0)
             assert (Ob[b, :, h:] == 0).all()  # pad heads untouched
@@ -211,5 +217,70 @@ def test_merge_random_problems(E, parts, nq, h, d, bf16, empty_frac, seed):
         want, wl = oattn.merge(o, lse)
         assert_parity(val(O) if bf16 else O, want, "bf16" if bf16 else "fp32", "merge")
         np.testing.assert_allclose(L, wl, atol=1e-5, rtol=1e-6)
+    finally:
+        E.free_all()
+
+
+@settings(max_examples=20, **SETTINGS)
+@given(n=st.integers(1, 300), h=st.integers(1, 6), d=st.sampled_from([64, 128]), bf16=st.booleans(),
+       cut=st.tuples(st.integers(0, 64), st.integers(0, 64)), pad=st.integers(0, 3),
+       pmax=st.sampled_from([10.0, 2e4]), theta=st.sampled_from([1e4, 5e5]), seed=st.integers(0, 10 ** 6))
+def test_mrope_random_problems(E, n, h, d, bf16, cut, pad, pmax, theta, seed):
+    """Standalone mRoPE on a padded [N, H, D] view: any split of the D/2
+    pairs into t / h / w sections, positions up to 2e4 (DM times)."""
+    E.config(False, False)
+    half = d // 2
+    a, b = sorted(min(c, half) for c in cut)
+    secs = (a, b - a, half - b)
+    r = np.random.default_rng(seed)
+    try:
+        x = r.standard_normal((n, h, d)).astype(np.float32)
+        x = val(bits_of(x)) if bf16 else x
+        pos = np.floor(r.uniform(0, pmax, (n, 3))).astype(np.float32)
+        X = E.empty((n, h + pad, d), np.uint16 if bf16 else np.float32)
+        X[:, :h] = bits_of(x) if bf16 else x
+        view = X[:, :h]
+        el = _el(view)
+        st_ = E.call("mrope_apply", emu_lib.ptr(view), BF16 if bf16 else FP32, n, h, d, el[0], el[1],
+                     emu_lib.ptr(E.array(pos)), *secs, ctypes.c_float(theta), None)
+        assert st_ == 0
+        want = omrope.apply(x, pos, secs, float(np.float32(theta)))
+        assert_parity(val(X[:, :h]) if bf16 else X[:, :h], want, "bf16" if bf16 else "fp32", "mrope")
+        assert (X[:, h:] == 0).all()
+    finally:
+        E.free_all()
+
+
+@settings(max_examples=20, **SETTINGS)
+@given(n=st.integers(1, 5000), bf16=st.booleans(), guided=st.booleans(), mirror=st.booleans(),
+       w=st.sampled_from([0.0, 1.0, 3.0, 7.5]), sig=st.tuples(st.floats(0, 1), st.floats(0, 1)),
+       seed=st.integers(0, 10 ** 6))
+def test_euler_random_problems(E, n, bf16, guided, mirror, w, sig, seed):
+    E.config(False, False)
+    s0, s1 = float(np.float32(max(sig))), float(np.float32(min(sig)))
+    r = np.random.default_rng(seed)
+    try:
+        x0 = r.standard_normal(n).astype(np.float32)
+        vc = r.standard_normal(n).astype(np.float32)
+        vb = r.standard_normal(n).astype(np.float32)
+        if bf16:
+            vc, vb = val(bits_of(vc)), val(bits_of(vb))
+        code = BF16 if bf16 else FP32
+        X = E.array(x0)
+        XB = E.empty((n,), np.uint16) if mirror else None
+        VC = E.array(bits_of(vc) if bf16 else vc)
+        VB = E.array(bits_of(vb) if bf16 else vb)
+        if guided:
+            st_ = E.call("flow_cfg_euler_step", emu_lib.ptr(X), emu_lib.ptr(VC), emu_lib.ptr(VB), code, n,
+                         ctypes.c_float(w), ctypes.c_float(s0), ctypes.c_float(s1), emu_lib.ptr(XB), None)
+            want = ocfg.euler_step(x0, vc, vb, w, s0, s1)
+        else:
+            st_ = E.call("flow_euler_step", emu_lib.ptr(X), emu_lib.ptr(VC), code, n, ctypes.c_float(s0),
+                         ctypes.c_float(s1), emu_lib.ptr(XB), None)
+            want = oeuler.step(x0, vc, s0, s1)
+        assert st_ == 0
+        assert_parity(X, want, "fp32", "euler")
+        if mirror:
+            np.testing.assert_array_equal(XB, W.bf16_bits(np.array(X)))
     finally:
         E.free_all()
