@@ -63,8 +63,13 @@ def attn_problem(draw):
         n_ar = 0
     return dict(d=d, h=h, hk=hk, mask=mask, nq=nq, nk=nk, q0=q0, n_ar=n_ar, n_prefix=n_prefix, cl=cl,
                 batch=draw(st.integers(1, 2)), pad=draw(st.integers(0, 2)),
-                std=draw(st.sampled_from([0.5, 1.0, 2.0])), rope=draw(st.booleans()),
-                scale=draw(st.sampled_from([0.0, 0.0, 0.04, 0.3])),
+                # (input std, softmax scale; 0 = 1/sqrt(D)): score std up to
+                # about 4, the regime of the bf16 contract (the workloads'
+                # N(0, 1) inputs at 1/sqrt(D) give 1; far more peaked rows
+                # make bf16 P alone move O by ~2e-2)
+                **dict(zip(("std", "scale"), draw(st.sampled_from(
+                    [(0.5, 0.0), (1.0, 0.0), (2.0, 0.0), (0.5, 0.04), (1.0, 0.04), (0.5, 0.3), (1.0, 0.3)])))),
+                rope=draw(st.booleans()),
                 mode=draw(st.sampled_from([(False, False), (True, True), (True, False), (True, 2)])),
                 seed=draw(st.integers(0, 10 ** 6)))
 
