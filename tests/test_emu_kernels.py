@@ -712,3 +712,29 @@ def test_planted_mistake_is_caught(tmp_path, what, patches, kind):
         assert any(caught), what
     finally:
         Ep.free_all()
+
+
+# ---------------------------------------------------------------------------
+def test_results_do_not_depend_on_scheduling(E):
+    """Every kernel's output is the same bits whatever the wave order between
+    barriers and whenever the LDS-DMA copies land (no result depends on
+    timing: no atomics, no order-dependent reductions across waves)."""
+    modes = [(False, False), (True, True), (True, 2), (False, 2)]
+    nq, h, hk, d = 260, 8, 2, 128
+    q, k, v = _qkv(70, nq, nq, h, hk, d, "bf16")
+    x, wa, wd = _gemm_inputs((300, 130, 128, 192), "bf16", seed=71)
+    outs = []
+    for mode in modes:
+        E.config(*mode)
+        Q, K, V = E.array(q.bits), E.array(k.bits), E.array(v.bits)
+        O, L = E.empty((nq, h, d), np.uint16), E.empty((h, nq), np.float32)
+        attention(E, Q, K, V, O, mode=AR, n_ar=90, lse=L)
+        O2 = E.empty((nq, h, d), np.uint16)
+        attention(E, Q, K, V, O2, mode=CH, q0=40, n_prefix=40, chunk_len=50)
+        Y = E.empty((300, 192), np.uint16)
+        region_linear(E, E.array(x.bits), E.array(wa.bits), E.array(wd.bits), Y, 130, BF16, BF16, 1)
+        outs.append([np.array(t) for t in (O, L, O2, Y)])
+        E.free_all()
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            np.testing.assert_array_equal(a.view(np.uint8), b.view(np.uint8))
