@@ -194,6 +194,11 @@ std::string where(const Worker* w) {
   siglongjmp(w->jb, 1);
 }
 
+// A fault inside a kernel (a work-item's own memory access, or the
+// emulator reading a copy's source for it) ends that launch.  The handler is
+// not async-signal-safe in general (it formats a message and takes a
+// mutex); it only runs for synchronous faults of kernel code, which holds no
+// lock and does not allocate.
 void on_fault(int sig, siginfo_t* si, void*) {
   Worker* w = W;
   if (w && w->in_kernel) {
@@ -497,11 +502,17 @@ void worker_main(Launch* L) {
   sigaltstack(&ss, nullptr);
   w->n_items = (int)(L->block.x * L->block.y * L->block.z);
   size_t tot;
+  bool mapped = true;
   for (int t = 0; t < w->n_items; ++t) {
     unsigned char* m = map_guarded(STACK, &tot);
-    w->stacks[t] = m + (size_t)sysconf(_SC_PAGESIZE);
+    mapped = mapped && m;
+    w->stacks[t] = m ? m + (size_t)sysconf(_SC_PAGESIZE) : nullptr;
   }
   w->lds_map = map_guarded(LDS_MAX, &w->lds_map_size);
+  if (!mapped || !w->lds_map) {
+    record("emulator: out of memory for work-item stacks or LDS");
+    L->failed = true;
+  }
   const size_t pg = (size_t)sysconf(_SC_PAGESIZE);
   const size_t body = (LDS_MAX + pg - 1) / pg * pg;
   w->lds_size = (L->shmem + 15) / 16 * 16;
@@ -523,8 +534,8 @@ void worker_main(Launch* L) {
     }
   }
   for (int t = 0; t < w->n_items; ++t)
-    munmap(w->stacks[t] - (size_t)sysconf(_SC_PAGESIZE), (STACK + pg - 1) / pg * pg + 2 * pg);
-  munmap(w->lds_map, w->lds_map_size);
+    if (w->stacks[t]) munmap(w->stacks[t] - pg, (STACK + pg - 1) / pg * pg + 2 * pg);
+  if (w->lds_map) munmap(w->lds_map, w->lds_map_size);
   ss.ss_flags = SS_DISABLE;
   sigaltstack(&ss, nullptr);
   free(w->altstack);
