@@ -337,13 +337,21 @@ void exec_op(Worker* w, int wave, uint64_t mask, int op) {
           A[l % 32][8 * (l / 32) + e] = bf(get<uint16_t>(L[l], 2 * e));
           B[8 * (l / 32) + e][l % 32] = bf(get<uint16_t>(L[l], 16 + 2 * e));
         }
+      // S = A B, summed over k in ascending order for every (i, j); the
+      // j loop runs over contiguous doubles
+      double S[32][32];
+      for (int i = 0; i < 32; ++i) {
+        for (int j = 0; j < 32; ++j) S[i][j] = 0.0;
+        for (int k = 0; k < 16; ++k) {
+          const double a = A[i][k];
+          for (int j = 0; j < 32; ++j) S[i][j] += a * B[k][j];
+        }
+      }
       float D[64][16];
       for (int l = 0; l < 64; ++l)
         for (int r = 0; r < 16; ++r) {
           const int i = 8 * (r / 4) + 4 * (l / 32) + r % 4, j = l % 32;
-          double s = 0.0;
-          for (int k = 0; k < 16; ++k) s += A[i][k] * B[k][j];
-          D[l][r] = (float)(s + (double)get<float>(L[l], 32 + 4 * r));
+          D[l][r] = (float)(S[i][j] + (double)get<float>(L[l], 32 + 4 * r));
         }
       for (int l = 0; l < 64; ++l) memcpy(L[l].out, D[l], 64);
       g_stats[ST_MFMA]++;
