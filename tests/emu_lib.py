@@ -53,9 +53,17 @@ def transform(name: str, src: str) -> str:
     return src
 
 
-def build(out_dir: str, dma_gemm: bool = False, jobs: int = 8, patches=()) -> str:
+UBSAN_LIB_DIR = "/opt/rocm/llvm/lib/clang/22/lib/linux"
+
+
+def build(out_dir: str, dma_gemm: bool = False, jobs: int = 8, patches=(), ubsan=None) -> str:
     """Builds the emulated library in out_dir; `patches` are (file, old,
-    new) text replacements applied first (to plant a mistake in a copy)."""
+    new) text replacements applied first (to plant a mistake in a copy).
+    With ubsan (default: the MOT_EMU_UBSAN environment variable) the kernel
+    sources and the emulator are built with UndefinedBehaviorSanitizer,
+    aborting at the first report."""
+    if ubsan is None:
+        ubsan = os.environ.get("MOT_EMU_UBSAN") == "1"
     os.makedirs(out_dir, exist_ok=True)
     # the sources include "../../include/motattn.h": keep that layout
     src_dir = os.path.join(out_dir, "pkg", "csrc")
@@ -79,6 +87,10 @@ def build(out_dir: str, dma_gemm: bool = False, jobs: int = 8, patches=()) -> st
              "-I", os.path.join(ROOT, "include"), "-I", src_dir]
     if dma_gemm:
         flags.append("-DMOT_GEMM_DMA=1")
+    link = []
+    if ubsan:
+        flags += ["-fsanitize=undefined", "-fno-sanitize-recover=all", "-g"]
+        link = ["-fsanitize=undefined", "-shared-libsan", "-Wl,-rpath," + UBSAN_LIB_DIR]
     cmds, objs = [], []
     for f in sorted(os.listdir(src_dir)):
         if f.endswith((".hip", ".cpp")):
@@ -97,7 +109,7 @@ def build(out_dir: str, dma_gemm: bool = False, jobs: int = 8, patches=()) -> st
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(run, cmds))
     lib = os.path.join(out_dir, "libmotattn_emu.so")
-    run([CXX, "-shared", "-fPIC", "-o", lib, *objs, "-lpthread"])
+    run([CXX, "-shared", "-fPIC", "-o", lib, *objs, "-lpthread", *link])
     return lib
 
 
