@@ -11,7 +11,9 @@ head mapping, batching, epilogues and reductions of each kernel are checked
 with no GPU.  Two run modes cover scheduling: LDS-DMA copies landing at once
 with waves run in order, and copies held back until the issuing wave's
 vmcnt wait (their LDS slots reading NaN meanwhile) with waves run in
-reverse.  A planted mistake in a copy of the sources (a missing wait, a
+reverse; a third, a seeded random wave order in every phase between
+barriers, is drawn by tests/test_emu_fuzz.py and by the check that results
+are the same bits in every mode.  A planted mistake in a copy of the sources (a missing wait, a
 missing barrier, a wrong key/value head, an unclamped ragged tile) must make
 these checks fail.
 
