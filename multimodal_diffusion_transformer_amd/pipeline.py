@@ -29,6 +29,11 @@ QKV, output projection and MLP) over the packed rows:
     A  = GELU(U2 W_up)                  mot_region_linear (GELU)
     H2 = H1 + A W_down                  mot_region_linear (residual add)
 
+``sample`` is the generation loop (§7.3) over a flow-shifted noise
+schedule (§6.3 shift map; §12.1 recommended steps and shift per mode): the
+noise levels come from mot_sigma_schedule and each consecutive pair drives
+one step of a DenoiserStep or GuidedDenoiserStep.
+
 ``StreamState`` is the rolling key/value cache of the streaming mode
 ("流式生成如何工作"): [AR prefix | ring of history frame slots | current
 chunk], keys stored rotated.
@@ -199,6 +204,18 @@ class GuidedDenoiserStep:
         self.attention()
         self.project_o()
         self.euler(sigma, sigma_next)
+
+
+def sample(stepper, n_steps, shift):
+    """Runs ``stepper.step(sigma_k, sigma_{k+1})`` for k = 0 .. n_steps - 1
+    over the schedule sigma_0 = 1 .. sigma_n = 0 that mot_sigma_schedule
+    builds for ``shift`` (shift 1 is the linear schedule).  ``stepper`` is a
+    DenoiserStep or GuidedDenoiserStep; its latent ends at sigma = 0.
+    Returns the float32 schedule that was used."""
+    sig = B.mot_sigma_schedule(n_steps, shift)
+    for k in range(int(n_steps)):
+        stepper.step(float(sig[k]), float(sig[k + 1]))
+    return sig
 
 
 class BlockStep:

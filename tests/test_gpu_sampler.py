@@ -1,0 +1,154 @@
+"""GPU sampler loops over the flow-shifted noise schedule ("Cosmos 3 方法原理全解"
+§6.3 shift map, §7.3 generation loop, §12.1 recommended steps, guidance and
+shift per mode).
+
+pipeline.sample takes the noise levels from mot_sigma_schedule (host) and
+runs one denoiser step per consecutive pair.  Checked here:
+
+* the schedule it walks is the oracle's (oracle.schedule, rounded once to
+  fp32), bit for bit, and every step receives the pair (sigma_k,
+  sigma_{k+1}) of it in order;
+* every step, end to end from the GPU's own latent (teacher forced), against
+  the oracle's step at that pair: the guided step (oracle.cfg.step) for the
+  robot-policy setting (4 steps, guidance 3, shift 5), on the tiny fp32 and
+  the policy bf16 workloads; the plain step (oracle.denoiser.step) for the
+  forward/inverse-dynamics setting (guidance 1, so the guided velocity is the
+  conditioned one, shift 5), over all 50 steps on the tiny fp32 workload;
+* the tiny workload's whole 50-step trajectory, run free, against the
+  oracle's own loop over the same schedule.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import cfg as ocfg
+from oracle import denoiser as oden
+from oracle import layout as olayout
+from oracle import schedule as osched
+from tests.gpu_util import assert_parity, device, say, to_np
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _setting(mode):
+    with open(os.path.join(HERE, "golden", "recommended_sampler_settings.json")) as f:
+        for s in json.load(f)["settings"]:
+            if s["mode"] == mode:
+                return s["steps"], s["guidance"][0], s["shift"]
+    raise KeyError(mode)
+
+
+def _pipeline():
+    from multimodal_diffusion_transformer_amd import pipeline
+    return pipeline
+
+
+def _oracle_schedule(n, shift):
+    return np.asarray(osched.shifted_schedule(n, shift), np.float64).astype(np.float32)
+
+
+def _weights(wl):
+    hid, h, d, hk = wl.hidden, wl.n_heads, wl.head_dim, wl.kv_heads
+    width = (h + 2 * hk) * d
+    return [W.make(wl.wid, W.T_WQKV_AR, (hid, width), wl.dtype, 0.02),
+            W.make(wl.wid, W.T_WQKV_DM, (hid, width), wl.dtype, 0.02),
+            W.make(wl.wid, W.T_WO_AR, (h * d, hid), wl.dtype, 0.02),
+            W.make(wl.wid, W.T_WO_DM, (h * d, hid), wl.dtype, 0.02)]
+
+
+class _Checked:
+    """Wraps a denoiser step: snapshots its inputs, runs the step, and hands
+    both to `check` with the step's index and noise levels."""
+
+    def __init__(self, inner, snap, check):
+        self.inner, self.snap, self.check, self.pairs = inner, snap, check, []
+
+    def step(self, sigma, sigma_next):
+        before = self.snap(self.inner)
+        self.inner.step(sigma, sigma_next)
+        torch.cuda.synchronize()
+        self.check(len(self.pairs), sigma, sigma_next, before)
+        self.pairs.append((sigma, sigma_next))
+
+
+def _assert_walked(sig, pairs, n, shift):
+    want = _oracle_schedule(n, shift)
+    np.testing.assert_array_equal(sig.view(np.uint32), want.view(np.uint32))
+    assert pairs == [(float(want[k]), float(want[k + 1])) for k in range(n)]
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "policy_bf16"])
+def test_guided_loop_robot_policy_setting(name):
+    dev = device()
+    P = _pipeline()
+    n_steps, guidance, shift = _setting("Nano policy (DROID)")
+    wl = W.BY_NAME[name]
+    n, hid, h, d, hk = wl.n_tokens, wl.hidden, wl.n_heads, wl.head_dim, wl.kv_heads
+    n_ar, n_clean, n_noisy = W.region_counts(wl.segments)
+    X = W.make(wl.wid, W.T_X, (n, hid), wl.dtype)
+    Xb = W.make(wl.wid, W.T_X_BASE, (n_ar, hid), wl.dtype)
+    ws = _weights(wl)
+    x0 = W.make(wl.wid, W.T_LATENT, (n_noisy, hid), "fp32")
+    g = P.GuidedDenoiserStep(wl, W.to_torch(X)[:n_ar], W.to_torch(Xb), W.to_torch(X)[n_ar:n_ar + n_clean],
+                             *(W.to_torch(w) for w in ws), torch.from_numpy(x0.f32.copy()), guidance,
+                             device=dev)
+    pos, _, n_ar_ = olayout.build(wl.segments)
+    assert n_ar_ == n_ar
+    wf = [w.f32 for w in ws]
+    tol = "bf16" if wl.dtype == "bf16" else "fp32"
+    store = "bf16" if tol == "bf16" else None
+
+    def check(k, s, sn, before):
+        x_in, Xdm_in = before
+        say("guided loop %s step %d: sigma %.6f -> %.6f" % (name, k, s, sn))
+        ref = ocfg.step(x_in, X.f32[:n_ar], Xb.f32, X.f32[n_ar:n_ar + n_clean], *wf, pos, n_ar, h, d,
+                        wl.sections, wl.theta, guidance, s, sn, x_as_input=Xdm_in[n_clean:], store=store,
+                        n_kv_heads=hk)
+        assert_parity(to_np(g.x), ref["x_next"], tol, "guided step %d x_next" % k)
+
+    run = _Checked(g, lambda s: (to_np(s.x), to_np(s.Xdm)), check)
+    sig = P.sample(run, n_steps, shift)
+    _assert_walked(sig, run.pairs, n_steps, shift)
+    assert run.pairs[-1][1] == 0.0
+
+
+def test_plain_loop_dynamics_setting_50_steps():
+    """Guidance 1 makes the guided velocity the conditioned one, so the
+    forward/inverse-dynamics setting runs the plain step."""
+    dev = device()
+    P = _pipeline()
+    n_steps, guidance, shift = _setting("Nano/Super forward/inverse dynamics")
+    assert guidance == 1
+    wl = W.BY_NAME["tiny_fp32"]
+    n, hid, h, d = wl.n_tokens, wl.hidden, wl.n_heads, wl.head_dim
+    n_noisy = W.region_counts(wl.segments)[2]
+    X = W.make(wl.wid, W.T_X, (n, hid), wl.dtype)
+    ws = _weights(wl)
+    x0 = W.make(wl.wid, W.T_LATENT, (n_noisy, hid), "fp32")
+    den = P.DenoiserStep(wl, W.to_torch(X), *(W.to_torch(w) for w in ws), torch.from_numpy(x0.f32.copy()),
+                         device=dev)
+    pos, _, n_ar = olayout.build(wl.segments)
+    wf = [w.f32 for w in ws]
+    Xc = X.f32[:n - n_noisy]
+
+    def check(k, s, sn, x_in):
+        ref = oden.step(x_in, Xc, *wf, pos, n_ar, h, d, wl.sections, wl.theta, s, sn)
+        if k % 10 == 0 or k == n_steps - 1:
+            say("plain loop step %d: sigma %.6f -> %.6f" % (k, s, sn))
+        assert_parity(to_np(den.x), ref["x_next"], "fp32", "plain step %d x_next" % k)
+
+    run = _Checked(den, lambda s: to_np(s.x), check)
+    sig = P.sample(run, n_steps, shift)
+    _assert_walked(sig, run.pairs, n_steps, shift)
+    # the whole trajectory run free against the oracle's own loop
+    x = x0.f32.astype(np.float64)
+    for k in range(n_steps):
+        x = oden.step(x, Xc, *wf, pos, n_ar, h, d, wl.sections, wl.theta, float(sig[k]),
+                      float(sig[k + 1]))["x_next"]
+    assert_parity(to_np(den.x), x, "fp32", "50-step trajectory")
