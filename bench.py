@@ -95,7 +95,9 @@ def attention_kernel_hash(lib_path=LIB_PATH):
     """First 16 hex digits of a sha256 over the gfx950 machine code and
     kernel descriptors of the attention kernels in the built library, or
     None if the library cannot be read.  It changes exactly when those
-    kernels do, and not with comments or host code."""
+    kernels do, and not with comments, host code or where the kernels sit in
+    their code object (a descriptor's bytes 16..23 hold the offset of its
+    kernel's code from the descriptor, which is masked)."""
     import hashlib
     import struct
 
@@ -109,7 +111,10 @@ def attention_kernel_hash(lib_path=LIB_PATH):
         return None
     h = hashlib.sha256()
     for name, off, size in sorted(spans):
-        h.update(name + b"\0" + struct.pack("<Q", size) + so[off:off + size])
+        body = bytearray(so[off:off + size])
+        if name.endswith(b".kd") and size >= 24:
+            body[16:24] = bytes(8)
+        h.update(name + b"\0" + struct.pack("<Q", size) + bytes(body))
     return h.hexdigest()[:16]
 
 

@@ -174,8 +174,10 @@ mot_status mot_layernorm_region(const void* x, void* y, int64_t n_rows, int64_t 
  * (x_k, x_{k+P}) by a = pos[axis(k)] * theta^(-2k/head_dim), axis = t for
  * k < sec_t, h for k < sec_t+sec_h, w otherwise.  Angles and their cos/sin
  * are evaluated in fp64, the rotation in fp32, the store rounds RNE.
- * head_dim in {64, 128}; sec_t+sec_h+sec_w == head_dim/2; all >= 0.
- * n_tok == 0 is a no-op.  Dispatch limit: n_tok * head_dim/8 <= 2^32 - 256. */
+ * head_dim in {64, 80, 128}; sec_t+sec_h+sec_w == head_dim/2; all >= 0.
+ * n_tok == 0 is a no-op.  Dispatch limit: head_dim/8 lanes per token,
+ * floor(256 / (head_dim/8)) tokens per 256-lane workgroup, at most
+ * 2^24 - 1 workgroups. */
 mot_status mrope_apply(void* x, int32_t dt, int64_t n_tok, int32_t n_heads, int32_t head_dim,
                        int64_t tok_stride, int64_t head_stride, const float* pos_thw,
                        int32_t sec_t, int32_t sec_h, int32_t sec_w, float theta, void* stream);
@@ -190,7 +192,9 @@ mot_status mrope_apply(void* x, int32_t dt, int64_t n_tok, int32_t n_heads, int3
  * [n_batch][H][nq], natural-log sum-exp of the scaled scores.  q_pos / k_pos
  * (nullable, device fp32 [nq][3] / [nk][3]): when set, Q / K are rotated by
  * mRoPE (sec_*, theta) as their tiles are loaded; otherwise they are used as
- * given.  scale == 0 means 1/sqrt(D).
+ * given.  scale == 0 means 1/sqrt(D).  The bf16 kernel keeps D = 80 tiles
+ * in the D = 128 layout: its PV products cover dims 0..95 and only dims
+ * 0..79 are stored.
  *
  * Grouped key/value heads (method page §12.4 model table, Q / KV heads
  * 16/8, 32/8, 64/8): n_kv_heads = H_kv divides H; query head h reads
@@ -211,7 +215,7 @@ typedef struct {
   float* lse;
   int32_t dt;        /* mot_dtype of q, k, v and o */
   int32_t n_heads;
-  int32_t head_dim;  /* 64 or 128 */
+  int32_t head_dim;  /* 64, 128, or 80 (method page §12.4: Super's hidden 5120 over 64 heads) */
   int32_t mask;      /* mot_mask_mode */
   int64_t nq, nk, q0;
   int64_t q_ts, q_hs, k_ts, k_hs, v_ts, v_hs, o_ts, o_hs;
@@ -257,8 +261,8 @@ mot_status mot_attention_fwd(const mot_attn_args* args, void* stream);
  * of the union.  Element type dt (bf16 or fp32) for o_parts and o.  In
  * fp32: the max of the parts' LSE, their weights exp(L_b - max), the
  * weighted sum, then division by the weights' sum.  A part whose LSE is
- * -inf for a row (no key) gets weight 0.  1 <= n_parts <= 16; head_dim 64 or
- * 128; nq == 0 is a no-op.  One lane per (row, head, 8 dims): nq * H * D/8
+ * -inf for a row (no key) gets weight 0.  1 <= n_parts <= 16; head_dim 64,
+ * 80 or 128; nq == 0 is a no-op.  One lane per (row, head, 8 dims): nq * H * D/8
  * <= 2^32 - 256.  INVALID_ARG for null or misaligned pointers, bad strides,
  * counts or dtype; UNSUPPORTED past the dispatch limit. */
 mot_status mot_attention_merge(const void* o_parts, const float* lse_parts, int32_t n_parts,

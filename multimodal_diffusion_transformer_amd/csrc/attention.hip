@@ -36,6 +36,11 @@
 //  * Q (rotated by mRoPE on load when positions are given) lives in
 //    registers for the whole key loop.  K is used as given (rotated
 //    beforehand when positions apply).
+//  * Head dims 64 and 128, and 80 (the model table's largest model: hidden
+//    5120 over 64 query heads, method page §12.4).  D = 80 tiles are kept
+//    in the 128 layout (attn_tiles.hpp); its scores take 5 k-steps, its PV
+//    products 3 output tiles of 32 dims, the last one half padding that is
+//    never stored, so 10 score and 12 PV MFMAs share a step's schedule.
 //  * Softmax in fp32 in the log2 domain (scale*log2(e) folded into one FMA
 //    before exp2).  A row's reference is its exact max over its first tile
 //    (which always holds key 0); it moves only if a later tile's sum of P
@@ -204,14 +209,39 @@ __device__ __forceinline__ void rope_chunk_pair(const RopeTable& rt, const float
   hi = make_uint4(pack_bf16(y2[0], y2[1]), pack_bf16(y2[2], y2[3]), pack_bf16(y2[4], y2[5]), pack_bf16(y2[6], y2[7]));
 }
 
+// Rotate one row's chunk by mRoPE when its rotate-half partners, D/2 dims
+// away, lie in the other lane half (D = 80: D/2 is not a multiple of 16):
+// own holds dims d..d+7, part the dims D/2 above them (d < D/2) or below
+// them, loaded by this lane too; only own is rotated, with the same
+// arithmetic as rope_chunk_pair.
+template <int D>
+__device__ __forceinline__ void rope_chunk_half(const RopeTable& rt, const float* pp, int d, uint4& own,
+                                                const uint4& part) {
+  constexpr int P = D / 2;
+  const uint32_t ow[4] = {own.x, own.y, own.z, own.w};
+  const uint32_t pw[4] = {part.x, part.y, part.z, part.w};
+  const bool first = d < P;
+  const int k0 = first ? d : d - P;
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float cs, sn;
+    rope_cs(pp[rope_axis(rt, k0 + e)], rt.inv_freq[k0 + e], cs, sn);
+    const float xo = __uint_as_float((e & 1) ? (ow[e >> 1] & 0xFFFF0000u) : (ow[e >> 1] << 16));
+    const float xp = __uint_as_float((e & 1) ? (pw[e >> 1] & 0xFFFF0000u) : (pw[e >> 1] << 16));
+    y[e] = first ? __builtin_fmaf(xo, cs, -xp * sn) : __builtin_fmaf(xp, sn, xo * cs);
+  }
+  own = make_uint4(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]), pack_bf16(y[4], y[5]), pack_bf16(y[6], y[7]));
+}
+
 // Per-wave state of the key loop.
 template <int D>
 struct WaveState {
   static constexpr int KSTEPS = D / 16;       // MFMA k-steps over the head dim
-  static constexpr int DT = D / 32;           // 32-wide output tiles over the head dim
+  static constexpr int DT = (D + 31) / 32;    // 32-wide output tiles (D = 80: the third ends past D)
   static constexpr int NSM = NST * KSTEPS;    // score MFMAs per tile
   static constexpr int NPV = NST * 2 * DT;    // PV MFMAs per tile
-  static_assert(NSM == NPV, "score and PV MFMAs alternate one to one");
+  static_assert(D % 32 != 0 || NSM == NPV, "score and PV MFMAs alternate one to one");
   bf16x8_t qreg[KSTEPS];   // B operand of S^T = K Q^T
   uint32_t kaddr[KSTEPS];  // K operand offsets within a K tile
   uint32_t vaddr[DT];      // V^T operand offsets within a V tile
@@ -225,7 +255,7 @@ struct WaveState {
 template <int D>
 __device__ __forceinline__ bf16x8_t k_operand(const WaveState<D>& ws, const unsigned char* ktile, int n) {
   const int st = n / WaveState<D>::KSTEPS, s = n % WaveState<D>::KSTEPS;
-  return as_bf16x8(*reinterpret_cast<const uint4*>(ktile + ws.kaddr[s] + st * 32 * Lay<D>::ROWB));
+  return as_bf16x8(*reinterpret_cast<const uint4*>(ktile + ws.kaddr[s] + st * 32 * Lay<store_dim(D)>::ROWB));
 }
 
 // A operand (V^T, 32 dims x 8+8 keys) of PV MFMA n: key block n / (2 DT),
@@ -234,9 +264,10 @@ template <int D>
 __device__ __forceinline__ bf16x8_t v_operand(const WaveState<D>& ws, const unsigned char* vtile, int n) {
   constexpr int DT = WaveState<D>::DT;
   const int st = n / (2 * DT), dt = n % DT, t = (n / DT) % 2;
-  const unsigned char* base = vtile + ws.vaddr[dt] + (32 * st + 8 * t) * Lay<D>::ROWB;
+  constexpr int ROWB = Lay<store_dim(D)>::ROWB;
+  const unsigned char* base = vtile + ws.vaddr[dt] + (32 * st + 8 * t) * ROWB;
   s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base));
-  s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + 4 * Lay<D>::ROWB));
+  s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + 4 * ROWB));
   s16x8_t a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8_t, a8);
 }
@@ -248,9 +279,11 @@ __device__ __forceinline__ bf16x8_t v_operand(const WaveState<D>& ws, const unsi
 //   DO_E : the exponentials of this tile, P(j) = exp2(cur * c - m_ref)
 //          packed to bf16, and their lane sum (c = scale * log2(e)).
 // No stream depends on another inside a step, so the schedule alternates
-// score and PV MFMAs, spreads the VALU operations of the exponentials
-// evenly between them, and reads each MFMA's LDS operand PD MFMAs ahead.
-// A scheduling fence after every MFMA keeps that order.
+// score and PV MFMAs (with unequal counts, D = 80's 10 and 12, score MFMA
+// number floor(m NSM / NM) goes wherever that count steps), spreads the VALU
+// operations of the exponentials evenly between them, and reads each MFMA's
+// LDS operand PD MFMAs ahead.  A scheduling fence after every MFMA keeps
+// that order.
 template <int D, bool DO_S, bool DO_E, bool DO_PV>
 __device__ __forceinline__ void tile_step(WaveState<D>& ws, const unsigned char* ktile,
                                           const unsigned char* vtile, const f32x16_t (&cur)[NST],
@@ -263,8 +296,14 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const unsigned char*
   const f32x16_t zero16 = {};
   constexpr int PD = 2, NB = PD + 1;
   const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
-  auto is_s = [](int m) { return DO_S && (!DO_PV || (m % 2 == 0)); };
-  auto idx = [](int m) { return (DO_S && DO_PV) ? m / 2 : m; };
+  constexpr bool EVEN = WS::NSM == WS::NPV;
+  auto s_step = [](int m) { return (m + 1) * WS::NSM / NM != m * WS::NSM / NM; };
+  auto is_s = [&](int m) { return DO_S && (!DO_PV || (EVEN ? m % 2 == 0 : s_step(m))); };
+  auto idx = [&](int m) {
+    if (!(DO_S && DO_PV)) return m;
+    if (EVEN) return m / 2;
+    return s_step(m) ? m * WS::NSM / NM : m - m * WS::NSM / NM;
+  };
   bf16x8_t ops[NB];
 #pragma unroll
   for (int m = 0; m < PD && m < NM; ++m)
@@ -349,9 +388,13 @@ __device__ __forceinline__ f32x16_t block_scores(const AttnParams& p, const Wave
   for (int s = 0; s < KSTEPS; s += 2) {
     __builtin_amdgcn_sched_barrier(0);
     const uint4 a0 = *reinterpret_cast<const uint4*>(row + 16 * s + 8 * g);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(row + 16 * (s + 1) + 8 * g);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), ws.qreg[s], sc, 0, 0, 0);
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), ws.qreg[s + 1], sc, 0, 0, 0);
+    if (s + 1 < KSTEPS) {
+      const uint4 a1 = *reinterpret_cast<const uint4*>(row + 16 * (s + 1) + 8 * g);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), ws.qreg[s], sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a1), ws.qreg[s + 1], sc, 0, 0, 0);
+    } else {  // the last of an odd count (D = 80)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a0), ws.qreg[s], sc, 0, 0, 0);
+    }
   }
   if (partial) {
     const int rel = ws.lim - kbase - 32 * st - 16 * g;
@@ -414,12 +457,13 @@ __device__ __forceinline__ void overflow_tile(const AttnParams& p, WaveState<D>&
 template <int D, int W, bool ROPE_Q>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_mfma(AttnParams p) {
-  using L = Lay<D>;
+  constexpr int DS = store_dim(D);  // dims per stored tile row
+  using L = Lay<DS>;
   static_assert(W == 4, "only the 4-wave workgroup shape is built");
   static_assert(L::BYTES <= 65536, "LDS copies stay below 64 KB");
   constexpr int BM = 32 * W;
   constexpr int KSTEPS = D / 16;
-  constexpr int DT = D / 32;
+  constexpr int DT = (D + 31) / 32;
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* kring = smem;                  // K tiles (ring of 2)
   unsigned char* vring = smem + 2 * L::TILE_B;  // V tiles (ring of 2)
@@ -474,8 +518,19 @@ void attn_fwd_mfma(AttnParams p) {
     for (int s = 0; s < KSTEPS; ++s)
       raw[s] = row_ok ? *reinterpret_cast<const uint4*>(src + 16 * s + 8 * g) : make_uint4(0, 0, 0, 0);
     if (ROPE_Q && row_ok) {
+      if constexpr (D % 32 == 0) {  // a chunk's partners are in the same lane, KSTEPS / 2 chunks up
 #pragma unroll
-      for (int s = 0; s < KSTEPS / 2; ++s) rope_chunk_pair<D>(p.rope, p.q_pos + 3 * my_row, s, g, raw[s], raw[s + KSTEPS / 2]);
+        for (int s = 0; s < KSTEPS / 2; ++s) rope_chunk_pair<D>(p.rope, p.q_pos + 3 * my_row, s, g, raw[s], raw[s + KSTEPS / 2]);
+      } else {
+        uint4 part[KSTEPS];
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const int d = 16 * s + 8 * g;
+          part[s] = *reinterpret_cast<const uint4*>(src + (d < D / 2 ? d + D / 2 : d - D / 2));
+        }
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) rope_chunk_half<D>(p.rope, p.q_pos + 3 * my_row, 16 * s + 8 * g, raw[s], part[s]);
+      }
     }
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) ws.qreg[s] = as_bf16x8(raw[s]);
@@ -487,9 +542,9 @@ void attn_fwd_mfma(AttnParams p) {
 
   // ---- loop-invariant LDS read offsets ----
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) ws.kaddr[s] = k_read_off<D>(s, lane);
+  for (int s = 0; s < KSTEPS; ++s) ws.kaddr[s] = k_read_off<DS>(s, lane);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) ws.vaddr[dt] = v_read_off<D>(dt, lane);
+  for (int dt = 0; dt < DT; ++dt) ws.vaddr[dt] = v_read_off<DS>(dt, lane);
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll
@@ -572,6 +627,7 @@ void attn_fwd_mfma(AttnParams p) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int d0 = 32 * dt + 8 * rr + 4 * g;
+        if (D % 32 != 0 && d0 >= D) continue;  // the padding dims of the last tile
         uint2 w;
         w.x = pack_bf16(ws.oacc[dt][4 * rr + 0] * inv_l, ws.oacc[dt][4 * rr + 1] * inv_l);
         w.y = pack_bf16(ws.oacc[dt][4 * rr + 2] * inv_l, ws.oacc[dt][4 * rr + 3] * inv_l);
@@ -585,7 +641,7 @@ void attn_fwd_mfma(AttnParams p) {
 template <int D, bool RQ>
 static hipError_t launch_attn(const AttnParams& p, int n_batch, hipStream_t s) {
   constexpr int W = ATTN_WAVES;
-  constexpr int BYTES = Lay<D>::BYTES;
+  constexpr int BYTES = Lay<store_dim(D)>::BYTES;
   // Set the LDS size attribute once; concurrent first calls may both set it
   // (it is idempotent), and the flag itself is atomic.
   static std::atomic<bool> configured{false};
@@ -628,6 +684,7 @@ hipError_t attention_bf16_mfma(const mot_attn_args* a, const RopeTable& rt, hipS
   // K is used as given (the caller checks that no k_pos was passed)
   const bool rq = a->q_pos != nullptr;
   if (a->head_dim == 128) return rq ? launch_attn<128, true>(p, n_batch, s) : launch_attn<128, false>(p, n_batch, s);
+  if (a->head_dim == 80) return rq ? launch_attn<80, true>(p, n_batch, s) : launch_attn<80, false>(p, n_batch, s);
   return rq ? launch_attn<64, true>(p, n_batch, s) : launch_attn<64, false>(p, n_batch, s);
 }
 

@@ -144,6 +144,8 @@ hipError_t attention_f32_valu(const mot_attn_args* a, const RopeTable& rt, hipSt
   dim3 grid((unsigned)((a->nq + F32_BQ - 1) / F32_BQ), (unsigned)a->n_heads, (unsigned)n_batch);
   if (a->head_dim == 128)
     hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(64), 0, s, p);
+  else if (a->head_dim == 80)
+    hipLaunchKernelGGL(attn_fwd_f32<80>, grid, dim3(64), 0, s, p);
   else
     hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(64), 0, s, p);
   return hipGetLastError();

@@ -84,7 +84,7 @@ extern "C" mot_status mot_attention_merge(const void* o_parts, const float* lse_
                                           int64_t p_ts, int64_t p_hs, void* o, int64_t o_ts, int64_t o_hs,
                                           float* lse, int32_t dt, void* stream) {
   using namespace mot;
-  if (nq < 0 || n_heads <= 0 || (head_dim != 64 && head_dim != 128)) return MOT_ERR_INVALID_ARG;
+  if (nq < 0 || n_heads <= 0 || (head_dim != 64 && head_dim != 80 && head_dim != 128)) return MOT_ERR_INVALID_ARG;
   if (n_parts < 1 || n_parts > MERGE_MAX_PARTS) return MOT_ERR_INVALID_ARG;
   if (dt != MOT_BF16 && dt != MOT_FP32) return MOT_ERR_INVALID_ARG;
   if (nq == 0) return MOT_OK;

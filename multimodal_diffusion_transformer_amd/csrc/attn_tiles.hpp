@@ -14,6 +14,14 @@ namespace mot {
 constexpr int BN = 64;        // keys per tile
 constexpr int NST = BN / 32;  // 32-key MFMA blocks per tile
 
+// Head dimensions the kernel takes: 64, 128, and 80 (hidden 5120 over 64
+// query heads).  A tile row is stored with DS = store_dim(D) dims: 80 is
+// kept in the 128 geometry (256-byte rows, 16 chunks), whose copies, swizzles
+// and transposing reads are the ones already walked; its chunks 10..15 hold
+// duplicates of chunks 0..5 of the same row, which no score reads and whose
+// outputs (dims 80..95 of the third 32-dim tile) are not stored.
+__host__ __device__ constexpr int store_dim(int D) { return D == 80 ? 128 : D; }
+
 template <int D>
 struct Lay {
   static constexpr int CH = D / 8;          // 16-byte chunks per row
@@ -53,14 +61,15 @@ __host__ __device__ __forceinline__ int key_perm(int rho) { return 16 * ((rho >>
 //                 last key re-read the last key)
 template <int D, int W>
 struct TileAddr {
-  using L = Lay<D>;
+  static constexpr int DS = store_dim(D);
+  using L = Lay<DS>;
   static constexpr int PER_WAVE = L::NINSTR / W;
   static_assert(PER_WAVE >= 1 && L::NINSTR % W == 0, "loads per wave");
   // With RPI = 64 / CH rows per load, the swizzle bits that vary with the
   // load index are bit 2 of r at D = 128 (so only i & 1 matters) and none at
   // D = 64, or for V: the fast path's lane offset takes NVAR_K values for K
   // and one for V.
-  static constexpr int NVAR_K = D == 128 ? 2 : 1;
+  static constexpr int NVAR_K = DS == 128 ? 2 : 1;
 
   // tile row that lane `lane` of copy i of wave `wave` fills
   __host__ __device__ __forceinline__ static int row_of(int wave, int i, int lane) {
@@ -69,7 +78,14 @@ struct TileAddr {
   // logical chunk (16 bytes = 8 dims) that lane fills in row r
   template <bool IS_K>
   __host__ __device__ __forceinline__ static int chunk_of(int r, int lane) {
-    return (lane % L::CH) ^ (IS_K ? swz_k<D>(r) : swz_v<D>(r));
+    return (lane % L::CH) ^ (IS_K ? swz_k<DS>(r) : swz_v<DS>(r));
+  }
+  // chunk of the row in global memory that fills logical chunk c: c itself,
+  // or for a stored chunk past the head's D / 8 a duplicate from the start
+  // of the same row (in range, finite)
+  __host__ __device__ __forceinline__ static int src_chunk(int c) {
+    if constexpr (DS == D) return c;
+    else return c < D / 8 ? c : c - D / 8;
   }
   // element offset of a tile's base from the tensor pointer
   __host__ __device__ __forceinline__ static int64_t tile_base_el(int64_t kbase, int64_t ts, int head, int64_t hs) {
@@ -78,7 +94,7 @@ struct TileAddr {
   // fast path, lane part: rows within the load plus the chunk (loop-invariant)
   template <bool IS_K>
   __host__ __device__ __forceinline__ static uint32_t lane_off(int wave, int i, int lane, int64_t ts) {
-    return (uint32_t)((lane / L::CH) * ts * 2 + chunk_of<IS_K>(row_of(wave, i, lane), lane) * 16);
+    return (uint32_t)((lane / L::CH) * ts * 2 + src_chunk(chunk_of<IS_K>(row_of(wave, i, lane), lane)) * 16);
   }
   // bytes per RPI rows (wave-uniform)
   __host__ __device__ __forceinline__ static uint32_t row_bytes(int64_t ts) { return (uint32_t)(L::RPI * ts * 2); }
@@ -90,7 +106,7 @@ struct TileAddr {
   __host__ __device__ __forceinline__ static uint32_t ragged_off(int wave, int i, int lane, int64_t ts, int64_t last) {
     const int r = row_of(wave, i, lane);
     const int64_t rr = r > last ? last : r;  // never negative: the lane offset is unsigned
-    return (uint32_t)(rr * ts * 2 + chunk_of<IS_K>(r, lane) * 16);
+    return (uint32_t)(rr * ts * 2 + src_chunk(chunk_of<IS_K>(r, lane)) * 16);
   }
   // LDS byte offset within the tile that copy n writes for lane
   __host__ __device__ __forceinline__ static int lds_dst(int n, int lane) { return n * 1024 + 16 * lane; }

@@ -25,6 +25,8 @@ __global__ __launch_bounds__(256) void mrope_kernel(T* __restrict__ x, int64_t n
   constexpr int TPT = P / 4;              // lanes per token
   constexpr int TOK_PER_BLOCK = 256 / TPT;
   const int lane_in_tok = threadIdx.x % TPT;
+  // D = 80: 10 lanes per token leave the workgroup's last 6 lanes idle
+  if (256 % TPT != 0 && threadIdx.x >= TOK_PER_BLOCK * TPT) return;
   const int64_t tok = (int64_t)blockIdx.x * TOK_PER_BLOCK + threadIdx.x / TPT;
   if (tok >= n_tok) return;
   const int k0 = 4 * lane_in_tok;
@@ -97,7 +99,7 @@ extern "C" mot_status mrope_apply(void* x, int32_t dt, int64_t n_tok, int32_t n_
   if (n_tok < 0 || n_heads <= 0) return MOT_ERR_INVALID_ARG;
   if (n_tok == 0) return MOT_OK;
   if (!x || !pos_thw) return MOT_ERR_INVALID_ARG;
-  if (head_dim != 64 && head_dim != 128) return MOT_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 80 && head_dim != 128) return MOT_ERR_INVALID_ARG;
   if (sec_t < 0 || sec_h < 0 || sec_w < 0 || sec_t + sec_h + sec_w != head_dim / 2)
     return MOT_ERR_INVALID_ARG;
   if (dt != MOT_BF16 && dt != MOT_FP32) return MOT_ERR_INVALID_ARG;
@@ -106,18 +108,21 @@ extern "C" mot_status mrope_apply(void* x, int32_t dt, int64_t n_tok, int32_t n_
   if (((uintptr_t)x & 15) || ((uintptr_t)pos_thw & 3)) return MOT_ERR_INVALID_ARG;
   if (tok_stride % align || head_stride % align || tok_stride <= 0 || head_stride <= 0)
     return MOT_ERR_INVALID_ARG;
-  // head_dim/8 lanes per token, 256 per workgroup, within one dispatch's
-  // 2^32 - 1 work-items
-  if (n_tok > ((int64_t)UINT32_MAX - 255) / (head_dim / 8)) return MOT_ERR_UNSUPPORTED;
+  // head_dim/8 lanes per token, floor(256 / (head_dim/8)) tokens per
+  // 256-lane workgroup, within one dispatch's 2^32 - 1 work-items
+  const int64_t tpb = 256 / (head_dim / 8);
+  if ((n_tok + tpb - 1) / tpb > (int64_t)(UINT32_MAX / 256)) return MOT_ERR_UNSUPPORTED;
   RopeFreqs fr;
   for (int k = 0; k < head_dim / 2; ++k) fr.inv_freq[k] = pow((double)theta, -2.0 * k / head_dim);
   const int sec_th = sec_t + sec_h;
   hipStream_t s = (hipStream_t)stream;
   if (dt == MOT_BF16) {
     if (head_dim == 128) launch_rope<bf16_t, 128>(x, n_tok, n_heads, tok_stride, head_stride, pos_thw, sec_t, sec_th, fr, s);
+    else if (head_dim == 80) launch_rope<bf16_t, 80>(x, n_tok, n_heads, tok_stride, head_stride, pos_thw, sec_t, sec_th, fr, s);
     else launch_rope<bf16_t, 64>(x, n_tok, n_heads, tok_stride, head_stride, pos_thw, sec_t, sec_th, fr, s);
   } else {
     if (head_dim == 128) launch_rope<float, 128>(x, n_tok, n_heads, tok_stride, head_stride, pos_thw, sec_t, sec_th, fr, s);
+    else if (head_dim == 80) launch_rope<float, 80>(x, n_tok, n_heads, tok_stride, head_stride, pos_thw, sec_t, sec_th, fr, s);
     else launch_rope<float, 64>(x, n_tok, n_heads, tok_stride, head_stride, pos_thw, sec_t, sec_th, fr, s);
   }
   MOT_CHECK_LAUNCH();

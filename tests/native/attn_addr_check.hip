@@ -15,6 +15,10 @@
 //    accumulator register r of lane half g;
 //  * the transposing V reads give lane l dim 32 dt + l % 32 and keys
 //    16 (l / 32) + 8 t + 0..7 of block st, the keys the P operand holds.
+// D = 80 is stored in the 128 geometry: a stored chunk c past the row's 10
+// is copied from chunk c - 10 of the same row, so it stays inside the
+// row; score reads never reach it, and the V reads of dims 80..95 get
+// dims 0..15 of the same key.
 // Prints "ok <copies> <reads>" or the first mismatches; exit status 1 on any.
 #include <stdio.h>
 #include <stdlib.h>
@@ -42,8 +46,9 @@ struct View { int64_t nk, ts, hs; int h; int nb; int64_t bs, extent; };
 
 template <int D>
 struct Walk {
+  static constexpr int DS = store_dim(D);
   using A = TileAddr<D, 4>;
-  using L = Lay<D>;
+  using L = Lay<DS>;
   long copies = 0, reads = 0;
   std::vector<int64_t> key;  // per 16-byte LDS slot: the key it holds
   std::vector<int> dim;      // ... and its first dim
@@ -64,6 +69,8 @@ struct Walk {
           const int n = wave * A::PER_WAVE + i;
           const int r = A::row_of(wave, i, lane);
           const int c = A::template chunk_of<IS_K>(r, lane);
+          const int src = c < D / 8 ? c : c - D / 8;  // the row's chunk the slot holds
+          CHECK(src == A::src_chunk(c), "source chunk");
           uint64_t off;  // bytes from the tensor pointer
           int64_t exact;
           if (last >= BN - 1) {
@@ -71,19 +78,19 @@ struct Walk {
             const uint32_t lo = IS_K ? A::template lane_off<true>(wave, i % A::NVAR_K, lane, v.ts)
                                      : A::template lane_off<false>(wave, 0, lane, v.ts);
             CHECK((int64_t)rb == (int64_t)n * L::RPI * v.ts * 2, "rows bytes wrap");
-            exact = (int64_t)(lane / L::CH) * v.ts * 2 + (int64_t)c * 16;
+            exact = (int64_t)(lane / L::CH) * v.ts * 2 + (int64_t)src * 16;
             CHECK((int64_t)lo == exact, "lane offset wrap or load-index aliasing lane %d i %d", lane, i);
             off = (uint64_t)(base_el * 2) + rb + lo;
           } else {
             const uint32_t ro = A::template ragged_off<IS_K>(wave, i, lane, v.ts, last);
-            exact = (int64_t)(r > last ? last : r) * v.ts * 2 + (int64_t)c * 16;
+            exact = (int64_t)(r > last ? last : r) * v.ts * 2 + (int64_t)src * 16;
             CHECK((int64_t)ro == exact && exact >= 0, "ragged offset wrap");
             off = (uint64_t)(base_el * 2) + ro;
           }
           const int64_t k = kbase + (r > last ? last : r);
           CHECK(k >= 0 && k < v.nk, "key %lld out of range", (long long)k);
-          CHECK(c >= 0 && 8 * c + 8 <= D, "chunk %d", c);
-          const int64_t want = 2 * ((int64_t)b * v.bs + k * v.ts + (int64_t)head * v.hs + 8 * c);
+          CHECK(c >= 0 && 8 * c + 8 <= DS && src >= 0 && 8 * src + 8 <= D, "chunk %d", c);
+          const int64_t want = 2 * ((int64_t)b * v.bs + k * v.ts + (int64_t)head * v.hs + 8 * src);
           CHECK((int64_t)off == want, "address %llu != %lld (head %d kbase %lld lane %d)",
                 (unsigned long long)off, (long long)want, head, (long long)kbase, lane);
           CHECK(want >= 0 && want / 2 + 8 <= v.extent, "outside the buffer: element %lld of %lld",
@@ -92,11 +99,11 @@ struct Walk {
           CHECK(dst >= 0 && dst + 16 <= L::TILE_B, "lds dst %d", dst);
           const int srow = dst / L::ROWB, phys = (dst % L::ROWB) / 16;
           CHECK(srow == r, "lds row %d != %d", srow, r);
-          CHECK(phys == (c ^ (IS_K ? swz_k<D>(r) : swz_v<D>(r))), "swizzle");
+          CHECK(phys == (c ^ (IS_K ? swz_k<DS>(r) : swz_v<DS>(r))), "swizzle");
           const int slot = dst / 16;
           CHECK(key[slot] == -1, "slot written twice");
           key[slot] = k;
-          dim[slot] = 8 * c;
+          dim[slot] = 8 * src;
           ++copies;
         }
     for (size_t s = 0; s < key.size(); ++s) CHECK(key[s] != -1, "slot %zu never written", s);
@@ -114,7 +121,7 @@ struct Walk {
     for (int lane = 0; lane < 64; ++lane)
       for (int st = 0; st < NST; ++st)
         for (int s = 0; s < D / 16; ++s) {
-          const uint32_t a = k_read_off<D>(s, lane) + st * 32 * L::ROWB;
+          const uint32_t a = k_read_off<DS>(s, lane) + st * 32 * L::ROWB;
           CHECK(a % 16 == 0 && a + 16 <= (uint32_t)L::TILE_B, "k read %u", a);
           const int rho = lane & 31;
           const int r = 32 * st + key_perm(rho);
@@ -125,7 +132,7 @@ struct Walk {
   }
 
   void read_v(int64_t kbase, int64_t last) {
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < (D + 31) / 32; ++dt)
       for (int st = 0; st < NST; ++st)
         for (int t = 0; t < 2; ++t)
           for (int hh = 0; hh < 2; ++hh) {
@@ -133,7 +140,7 @@ struct Walk {
             int64_t seg_key[64];
             int seg_dim[64];
             for (int lane = 0; lane < 64; ++lane) {
-              const uint32_t a = v_read_off<D>(dt, lane) + (32 * st + 8 * t + 4 * hh) * L::ROWB;
+              const uint32_t a = v_read_off<DS>(dt, lane) + (32 * st + 8 * t + 4 * hh) * L::ROWB;
               CHECK(a % 8 == 0 && a + 8 <= (uint32_t)L::TILE_B, "v read %u", a);
               seg_key[lane] = key[a / 16];
               seg_dim[lane] = dim[a / 16] + 4 * ((a % 16) / 8);
@@ -148,7 +155,8 @@ struct Walk {
                 const int got_dim = seg_dim[src] + i % 4;
                 const int r = 32 * st + 16 * (lane >> 5) + 8 * t + 4 * hh + k;
                 CHECK(got_key == kbase + (r > last ? last : r), "V operand key (lane %d dt %d)", lane, dt);
-                CHECK(got_dim == 32 * dt + (lane & 31), "V operand dim (lane %d dt %d)", lane, dt);
+                const int want_dim = 32 * dt + (lane & 31);  // past D: a duplicate of dim - D
+                CHECK(got_dim == (want_dim < D ? want_dim : want_dim - D), "V operand dim (lane %d dt %d)", lane, dt);
                 ++reads;
               }
             }
@@ -207,6 +215,11 @@ int main(int argc, char** argv) {
       reads += w.reads;
     } else if (d == 64) {
       Walk<64> w;
+      w.run(v);
+      copies += w.copies;
+      reads += w.reads;
+    } else if (d == 80) {
+      Walk<80> w;
       w.run(v);
       copies += w.copies;
       reads += w.reads;

@@ -11,7 +11,7 @@ operand reads must give the keys and dims the MFMA layouts expect.  The walk
 covers every tile index up to ceil(nk / 64), so it covers every launch of
 that view in both mask modes and at any q0 and nq.
 
-Views: the five workloads (K and V as strided views of the packed
+Views: the workloads (K and V as strided views of the packed
 [N, 3, H, D] projection output; the streaming cache contiguous), ragged key
 counts around the tile size, head-major layouts, and the largest token
 stride the API accepts (64-row tiles below 4 GiB).  Planted mistakes in a
@@ -77,7 +77,7 @@ EDGE_NK = [1, 2, 63, 64, 65, 127, 128, 129, 300, 1030]
 
 def _edge_views():
     v = []
-    for d in (64, 128):
+    for d in (64, 80, 128):
         for nk in EDGE_NK:
             v.append((d, nk, 3 * 2 * d, d, 2))      # packed, 2 heads
             v.append((d, nk, 3 * d, d, 1))          # packed, 1 head
@@ -146,14 +146,16 @@ PLANTED = [
     # (what, pattern, replacement) applied to a copy of attn_tiles.hpp
     ("ragged rows not clamped", "const int64_t rr = r > last ? last : r;", "const int64_t rr = r;"),
     ("K copy without the swizzle the reads apply",
-     "return (lane % L::CH) ^ (IS_K ? swz_k<D>(r) : swz_v<D>(r));",
-     "return (lane % L::CH) ^ (IS_K ? 0 : swz_v<D>(r));"),
+     "return (lane % L::CH) ^ (IS_K ? swz_k<DS>(r) : swz_v<DS>(r));",
+     "return (lane % L::CH) ^ (IS_K ? 0 : swz_v<DS>(r));"),
     ("V swizzle ignored by the reads", "const int f = swz_v<D>(rowl);", "const int f = 0;"),
     ("row within a load off by one chunk", "return (wave * PER_WAVE + i) * L::RPI + lane / L::CH;",
      "return (wave * PER_WAVE + i) * L::RPI + lane / L::CH + (lane == 63);"),
     ("key_perm halves swapped", "16 * ((rho >> 2) & 1)", "16 * (1 - ((rho >> 2) & 1))"),
     ("row bytes in 16-bit arithmetic", "return (uint32_t)(L::RPI * ts * 2);",
      "return (uint32_t)(uint16_t)(L::RPI * ts * 2);"),
+    ("D = 80 padding chunks copied from past the row", "else return c < D / 8 ? c : c - D / 8;",
+     "else return c;"),
     ("head slots not spread by XCD", "return xcd_heads ? (hs & 7) * xcd_heads + (hs >> 3) : hs;",
      "return xcd_heads ? (hs % xcd_heads) * 8 + hs / xcd_heads : hs;"),
 ]
@@ -168,6 +170,6 @@ def test_planted_mistake_is_caught(tmp_path, what, pat, rep):
     (inc / "attn_tiles.hpp").write_text(src.replace(pat, rep))
     out = tmp_path / "aac"
     _build(out, str(inc))
-    views = [(128, 300, 9216, 128, 2), (64, 129, 768, 64, 2), (128, 70, MAX_TS, 128, 1)]
+    views = [(128, 300, 9216, 128, 2), (64, 129, 768, 64, 2), (128, 70, MAX_TS, 128, 1), (80, 300, 6400, 80, 2)]
     rc, text = _run(out, views, maps=[(32, 4)])
     assert rc != 0 and "FAIL" in text, what

@@ -54,8 +54,8 @@ def test_kernel_hash_tracks_the_attention_machine_code(tmp_path):
     so = open(bench.LIB_PATH, "rb").read()
     spans = bench.attention_kernel_spans(so)
     names = {n for n, _, _ in spans}
-    # bf16 kernel at D = 128 and 64, with and without Q rotation, and descriptors
-    assert len(spans) == 8 and sum(n.endswith(b".kd") for n in names) == 4
+    # bf16 kernel at D = 128, 80 and 64, with and without Q rotation, and descriptors
+    assert len(spans) == 12 and sum(n.endswith(b".kd") for n in names) == 6
     assert all(size > 0 for _, _, size in spans)
     h0 = bench.attention_kernel_hash()
     assert h0 is not None and len(h0) == 16
@@ -70,9 +70,13 @@ def test_kernel_hash_tracks_the_attention_machine_code(tmp_path):
     # a bit inside the first attention kernel changes the hash
     _, off, size = sorted(spans)[0]
     assert flipped(off + size // 2) != h0
-    # a bit of host code (the ELF .text of the library) does not
+    # a bit of host code (the ELF .text of the library) does not, nor the
+    # code-entry offset of a descriptor (where the kernel sits)
     text = next(x for x in bench._elf_sections(so) if x["name"] == ".text")
     assert flipped(text["off"] + text["size"] // 2) == h0
+    _, kd_off, _ = next(s for s in sorted(spans) if s[0].endswith(b".kd"))
+    assert flipped(kd_off + 17) == h0
+    assert flipped(kd_off + 24) != h0
     # an unreadable library gives no hash
     (tmp_path / "junk.so").write_bytes(b"not an elf")
     assert bench.attention_kernel_hash(str(tmp_path / "junk.so")) is None

@@ -45,7 +45,7 @@ def E(tmp_path_factory):
 
 @st.composite
 def attn_problem(draw):
-    d = draw(st.sampled_from([64, 128]))
+    d = draw(st.sampled_from([64, 80, 128]))
     hk = draw(st.integers(1, 4))
     h = hk * draw(st.integers(1, 4))
     mask = draw(st.sampled_from([AR, CH]))
@@ -127,7 +127,7 @@ def test_attention_bf16_random_problems(E, pr):
 
 
 @settings(max_examples=15 * SCALE, **SETTINGS)
-@given(d=st.sampled_from([64, 128]), hk=st.integers(1, 3), g=st.integers(1, 3), nq=st.integers(1, 120),
+@given(d=st.sampled_from([64, 80, 128]), hk=st.integers(1, 3), g=st.integers(1, 3), nq=st.integers(1, 120),
        extra=st.integers(0, 60), n_ar_frac=st.floats(0, 1), seed=st.integers(0, 10 ** 6))
 def test_attention_fp32_random_problems(E, d, hk, g, nq, extra, n_ar_frac, seed):
     E.config(False, True)
@@ -208,7 +208,7 @@ def test_layernorm_random_problems(E, hidden8, n, ar_frac, in_bf16, out_bf16, sc
 
 
 @settings(max_examples=20 * SCALE, **SETTINGS)
-@given(parts=st.integers(1, 16), nq=st.integers(1, 60), h=st.integers(1, 5), d=st.sampled_from([64, 128]),
+@given(parts=st.integers(1, 16), nq=st.integers(1, 60), h=st.integers(1, 5), d=st.sampled_from([64, 80, 128]),
        bf16=st.booleans(), empty_frac=st.floats(0, 0.5), seed=st.integers(0, 10 ** 6))
 def test_merge_random_problems(E, parts, nq, h, d, bf16, empty_frac, seed):
     E.config(False, False)
@@ -235,7 +235,7 @@ def test_merge_random_problems(E, parts, nq, h, d, bf16, empty_frac, seed):
 
 
 @settings(max_examples=20, **SETTINGS)
-@given(n=st.integers(1, 300), h=st.integers(1, 6), d=st.sampled_from([64, 128]), bf16=st.booleans(),
+@given(n=st.integers(1, 300), h=st.integers(1, 6), d=st.sampled_from([64, 80, 128]), bf16=st.booleans(),
        cut=st.tuples(st.integers(0, 64), st.integers(0, 64)), pad=st.integers(0, 3),
        pmax=st.sampled_from([10.0, 2e4]), theta=st.sampled_from([1e4, 5e5]), seed=st.integers(0, 10 ** 6))
 def test_mrope_random_problems(E, n, h, d, bf16, cut, pad, pmax, theta, seed):

@@ -131,6 +131,10 @@ CASES = [
     ("gqa_16_4_xcd_map", 140, 140, 0, AR, 50, 0, 0, 64, 16, 4),
     ("nano_heads_32_8", 100, 100, 0, AR, 30, 0, 0, 128, 32, 8),
     ("gqa_chunk", 2 * 64 + 9, 40 + 2 * 64 + 9, 40, CH, 0, 40, 64, 128, 8, 2),
+    ("ar_small_d80", 300, 300, 0, AR, 70, 0, 0, 80, 4, 4),
+    ("ar_qoffset_d80", 150, 333, 183, AR, 100, 0, 0, 80, 2, 2),
+    ("chunk_d80", 2 * 64 + 9, 40 + 2 * 64 + 9, 40, CH, 0, 40, 64, 80, 4, 2),
+    ("super_heads_64_8_d80", 100, 100, 0, AR, 30, 0, 0, 80, 64, 8),
 ]
 
 
@@ -174,7 +178,7 @@ def test_attention_bf16_strided_packed_views(E, mode):
 
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
-@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("d", [128, 64, 80])
 def test_attention_bf16_batched_heads_and_strides(E, mode, d):
     """Two batch items with their own Q, K, V, O, LSE (GQA 4 -> 2), against
     the oracle per item."""
@@ -222,7 +226,7 @@ def test_attention_key_split_and_merge(E, mode):
     np.testing.assert_allclose(L, lse, atol=BF16_LSE_ATOL, rtol=0)
 
 
-@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("d", [128, 64, 80])
 def test_attention_bf16_rope_q_on_load(E, d):
     E.config(True, True)
     wl = W.BY_NAME["policy_bf16"]
@@ -242,14 +246,14 @@ def test_attention_bf16_rope_q_on_load(E, d):
     assert_parity(val(O), want, "bf16", "rope on load")
 
 
-@pytest.mark.parametrize("kind", ["jump", "first_tile_low"])
-@pytest.mark.parametrize("hk", [2, 1])
-def test_attention_large_scores_move_the_reference(E, kind, hk):
+@pytest.mark.parametrize("kind,hk,d", [("jump", 2, 128), ("jump", 1, 128), ("first_tile_low", 2, 128),
+                                        ("first_tile_low", 1, 128), ("jump", 1, 80), ("first_tile_low", 2, 80)])
+def test_attention_large_scores_move_the_reference(E, kind, hk, d):
     """The rare path that recomputes a tile's scores from K in global memory
     (overflow of the tile sum past 2^64), with GQA and a second batch item so
-    that its K addressing uses both."""
+    that its K addressing uses both; at D = 80 its k-step count is odd."""
     E.config(True, True)
-    nq, n_ar, h, d = 400, 100, 2, 128
+    nq, n_ar, h = 400, 100, 2
     Qs, Ks, Vs, ins = [], [], [], []
     for b in range(2):
         q, k, v = _qkv(11 + b, nq, nq, h, hk, d, "bf16")
@@ -299,6 +303,7 @@ F32_CASES = [
     ("f32_chunk_d64", 3 * 37 + 5, 20 + 3 * 37 + 5, 20, CH, 0, 20, 37, 64, 3, 3),
     ("f32_chunk_d128", 2 * 45 + 7, 33 + 2 * 45 + 7, 33, CH, 0, 33, 45, 128, 2, 2),
     ("f32_gqa_d64", 90, 90, 0, AR, 30, 0, 0, 64, 6, 2),
+    ("f32_ar_d80", 110, 110, 0, AR, 40, 0, 0, 80, 4, 2),
 ]
 
 
@@ -337,12 +342,12 @@ def test_attention_fp32_batched_rope_both(E):
 # ---------------------------------------------------------------------------
 # merge
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
-@pytest.mark.parametrize("parts", [2, 3, 16])
-def test_merge(E, dt, parts):
+@pytest.mark.parametrize("parts,d", [(2, 64), (3, 64), (16, 64), (3, 80)])
+def test_merge(E, dt, parts, d):
     """Merge of per-part outputs through their LSE, with some parts holding
     no key for some rows (LSE -inf, NaN outputs that must not be read)."""
     E.config(False, False)
-    nq, h, d = 37, 3, 64
+    nq, h = 37, 3
     r = np.random.default_rng(parts)
     o = W.make(50 + parts, 1, (parts, nq, h, d), dt)
     lse = (r.standard_normal((parts, h, nq)) * 3).astype(np.float32)
@@ -572,7 +577,7 @@ def test_euler_guidance_one_and_zero_velocity(E):
 
 # ---------------------------------------------------------------------------
 # mRoPE
-@pytest.mark.parametrize("name", ["tiny_fp32", "policy_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "policy_bf16", "super_t2v480p_bf16"])
 def test_mrope_strided_views(E, name):
     E.config(False, False)
     wl = W.BY_NAME[name]
@@ -673,8 +678,11 @@ PLANTED = [
                                         "its slot", "")], "wrong"),
     ("wrong key/value head", [("attention.hip", "head / p.kv_group)", "head % (p.n_heads / p.kv_group))")],
      "wrong"),
-    ("K copy and read swizzles differ", [("attn_tiles.hpp", "(IS_K ? swz_k<D>(r) : swz_v<D>(r))",
-                                          "(IS_K ? 0 : swz_v<D>(r))")], "wrong"),
+    ("K copy and read swizzles differ", [("attn_tiles.hpp", "(IS_K ? swz_k<DS>(r) : swz_v<DS>(r))",
+                                          "(IS_K ? 0 : swz_v<DS>(r))")], "wrong"),
+    ("D = 80 padding dims stored", [("attention.hip", "if (D % 32 != 0 && d0 >= D) continue;", "")], "wrong80"),
+    ("D = 80 rotation partner on the wrong side", [("attention.hip", "(d < D / 2 ? d + D / 2 : d - D / 2)",
+                                                    "(d < D / 2 ? d + D / 2 : d)")], "rope80"),
     ("GEMM epilogue residual row", [("gemm.hip", "store4<OUT_BF16, EPI>(p, row * p.N + n, o);\n      }\n  }\n}\n\n//",
                                      "store4<OUT_BF16, EPI>(p, (row ^ 1) * p.N + n, o);\n      }\n  }\n}\n\n//")],
      "gemm"),
@@ -699,8 +707,19 @@ def test_planted_mistake_is_caught(tmp_path, what, patches, kind):
                     Y = Ep.empty((20, 8), np.float32)
                     region_linear(Ep, Ep.array(x.f32), Ep.array(wa.f32), None, Y, 20, FP32, FP32)
                     assert_parity(Y, oproj.project(x.f32, wa.f32, wa.f32, 20), "fp32", what)
+                elif kind == "rope80":
+                    n, h, d = 200, 2, 80
+                    pos = np.ascontiguousarray(olayout.build(W.BY_NAME["policy_bf16"].segments)[0][:n])
+                    secs = (10, 15, 15)
+                    q, k, v = _qkv(8, n, n, h, h, d, "bf16")
+                    kb = bits_of(omrope.apply(k.f32, pos, secs, 1e4))
+                    O = Ep.empty((n, h, d), np.uint16)
+                    attention(Ep, Ep.array(q.bits), Ep.array(kb), Ep.array(v.bits), O, mode=AR, n_ar=60,
+                              q_pos=Ep.array(pos), sections=secs, theta=1e4)
+                    want, _ = oattn.attention(omrope.apply(q.f32, pos, secs, 1e4), val(kb), v.f32, 0, AR, 60)
+                    assert_parity(val(O), want, "bf16", what)
                 else:
-                    nq, h, hk, d = 300, 8, 2, 128
+                    nq, h, hk, d = 300, 8, 2, 80 if kind == "wrong80" else 128
                     q, k, v = _qkv(7, nq, nq, h, hk, d, "bf16")
                     Q, K, V = Ep.array(q.bits), Ep.array(k.bits), Ep.array(v.bits)
                     O = Ep.empty((nq, h, d), np.uint16)

@@ -211,11 +211,13 @@ def test_block_forward_policy_layout_teacher_forced():
     assert rl <= BF16_REL_L2
 
 
-def test_block_forward_480p_sampled_rows():
-    """The whole layer at the grouped-head 480p workload (25,474 tokens,
-    hidden 4,096, FFN 12,288), each stage teacher-forced on sampled rows."""
+@pytest.mark.parametrize("name", ["nano_t2v480p_bf16", "super_t2v480p_bf16"])
+def test_block_forward_480p_sampled_rows(name):
+    """The whole layer at the grouped-head 480p workloads (25,474 tokens;
+    hidden 4,096, 32 / 8 heads of 128, FFN 12,288, and hidden 5,120, 64 / 8
+    heads of 80, FFN 25,600), each stage teacher-forced on sampled rows."""
     dev = device()
-    wl = W.BY_NAME["nano_t2v480p_bf16"]
+    wl = W.BY_NAME[name]
     blk, X, p = _block(wl, dev)
     pos, reg, n_ar = olayout.build(wl.segments)
     n, h, hk, d = blk.n, wl.n_heads, wl.kv_heads, wl.head_dim
@@ -248,7 +250,7 @@ def test_block_forward_480p_sampled_rows():
     blk.rope_k()
     blk.attention()
     torch.cuda.synchronize()
-    heads = [0, 7, 31]
+    heads = [0, 7, h - 1]
     kv = sorted({oattn.kv_head(x_, h, hk) for x_ in heads})
     kt = torch.tensor(kv, device=dev)
     Kall = to_np(blk.k.index_select(1, kt))

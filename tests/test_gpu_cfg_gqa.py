@@ -143,6 +143,9 @@ GQA_CASES = [
     ("bf16", 128, 16, 8, 2 * 45 + 7, 33 + 2 * 45 + 7, 33, CH),
     ("fp32", 64, 4, 1, 150, 150, 0, AR),
     ("fp32", 128, 4, 2, 97, 130, 33, CH),
+    ("bf16", 80, 64, 8, 200, 260, 60, AR),    # the model table's largest head shape
+    ("bf16", 80, 8, 2, 2 * 45 + 7, 33 + 2 * 45 + 7, 33, CH),
+    ("fp32", 80, 4, 2, 150, 150, 0, AR),
 ]
 
 
@@ -172,13 +175,15 @@ def test_attention_grouped_heads(case):
                        O2.view(torch.int16) if dtype == "bf16" else O2)
 
 
-def test_attention_grouped_heads_480p_sampled_rows():
-    """The grouped-head 480p workload (32 / 8 heads, 25,474 tokens): K and V
-    strided views of the fused [N, (32 + 16) 128] projection output, Q
-    rotated on load; sampled rows of 4 heads spanning 2 key/value heads."""
+@pytest.mark.parametrize("name", ["nano_t2v480p_bf16", "super_t2v480p_bf16"])
+def test_attention_grouped_heads_480p_sampled_rows(name):
+    """The grouped-head 480p workloads (32 / 8 heads of 128 and 64 / 8 heads
+    of 80, 25,474 tokens): K and V strided views of the fused
+    [N, (H + 2 H_kv) D] projection output, Q rotated on load; sampled rows of
+    4 heads spanning 2 key/value heads."""
     dev = device()
     mot = _mot()
-    wl = W.BY_NAME["nano_t2v480p_bf16"]
+    wl = W.BY_NAME[name]
     pos, reg, n_ar = olayout.build(wl.segments)
     n, h, hk, d = len(reg), wl.n_heads, wl.kv_heads, wl.head_dim
     say("attention GQA 480p n=%d %d/%d heads" % (n, h, hk))
@@ -197,7 +202,7 @@ def test_attention_grouped_heads_480p_sampled_rows():
     rng = np.random.default_rng(35)
     rows = np.unique(np.concatenate([np.arange(n_ar), np.arange(n_ar, n_ar + 64),
                                      rng.choice(np.arange(n_ar, n), 64, replace=False), [n - 1]]))
-    heads = [0, 3, 4, 31]
+    heads = [0, 3, h // hk, h - 1]
     kvh = [oattn.kv_head(x, h, hk) for x in heads]
     got = to_np(O.index_select(0, torch.from_numpy(rows).to(dev)))[:, heads]
     qr = omrope.apply(q.f32[rows], pos[rows], wl.sections, wl.theta)
@@ -313,11 +318,12 @@ def test_guided_step_teacher_forced(name, guidance, steps, checked):
                       "end-to-end x_next")
 
 
-def test_guided_step_grouped_heads_480p_sampled():
-    """The grouped-head 480p workload with guidance 6: one guided step,
+@pytest.mark.parametrize("name", ["nano_t2v480p_bf16", "super_t2v480p_bf16"])
+def test_guided_step_grouped_heads_480p_sampled(name):
+    """The grouped-head 480p workloads with guidance 6: one guided step,
     each stage teacher-forced on sampled rows and heads."""
     dev = device()
-    wl = W.BY_NAME["nano_t2v480p_bf16"]
+    wl = W.BY_NAME[name]
     g, X, Xb, ws, x = _guided_step(wl, wl.guidance, dev)
     pos, reg, n_ar = olayout.build(wl.segments)
     n, h, d, hk = g.n, wl.n_heads, wl.head_dim, wl.kv_heads

@@ -232,6 +232,9 @@ def test_launches_past_one_dispatch_are_unsupported():
     # mRoPE: 2^29 tokens x 16 lanes
     assert mot.raw_call("mrope_apply", vp(4096), 0, 1 << 29, 1, 128, 1024, 128, vp(4096), 16, 24,
                         24, ctypes.c_float(1e4), None) == mot.MOT_ERR_UNSUPPORTED
+    # mRoPE at D = 80: 25 tokens per 256-lane workgroup, at most 2^24 - 1 workgroups
+    assert mot.raw_call("mrope_apply", vp(4096), 0, 25 * ((1 << 24) - 1) + 1, 1, 80, 1024, 80, vp(4096), 10,
+                        15, 15, ctypes.c_float(1e4), None) == mot.MOT_ERR_UNSUPPORTED
     # projection: 2^31 rows x 2^16 columns of 128 x 128 tiles; fp32 d_out = 2^28
     assert mot.raw_call("mot_qkv_project", vp(4096), vp(4096), vp(4096), vp(4096), 1 << 31, 0, 64,
                         1 << 16, 0, 0, None) == mot.MOT_ERR_UNSUPPORTED

@@ -4,7 +4,7 @@ import pytest
 
 from oracle import mrope
 
-SECTIONS = {64: (8, 12, 12), 128: (16, 24, 24)}
+SECTIONS = {64: (8, 12, 12), 80: (10, 15, 15), 128: (16, 24, 24)}
 
 
 def _rope1d_complex(x, p, theta):
@@ -19,7 +19,7 @@ def _rope1d_complex(x, p, theta):
     return np.concatenate([z.real, z.imag], axis=-1)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 80, 128])
 def test_text_positions_reduce_to_1d_rope(d):
     rng = np.random.default_rng(1)
     n = 40
@@ -31,7 +31,7 @@ def test_text_positions_reduce_to_1d_rope(d):
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 80, 128])
 def test_relative_shift_invariance_at_dm_positions(d):
     rng = np.random.default_rng(2)
     n = 24

@@ -183,6 +183,15 @@ def _build() -> List[Workload]:
         hidden=4096, sections=(16, 24, 24), n_kv_heads=8, guidance=6.0, ffn=12288,
         segments=(text(512), *eos_bog(), video(DM_NOISY, 16, 1, 30, 52)),
         sigmas=(1.0, 0.975)))
+    # 7. Grouped heads at the model table's Super shape (64 query / 8
+    #    key-value heads, hidden 5120, so heads of 5120 / 64 = 80 dims; FFN
+    #    25600) on the same 480p text-to-video layout.  The 40 rotary pairs
+    #    split t / h / w as 10 / 15 / 15, the D = 128 split scaled.
+    w.append(Workload(
+        wid=6, name="super_t2v480p_bf16", dtype="bf16", n_heads=64, head_dim=80,
+        hidden=5120, sections=(10, 15, 15), n_kv_heads=8, guidance=6.0, ffn=25600,
+        segments=(text(512), *eos_bog(), video(DM_NOISY, 16, 1, 30, 52)),
+        sigmas=(1.0, 0.975)))
     return w
 
 
