@@ -160,6 +160,30 @@ def test_attention_bf16(E, case, mode):
 
 
 @pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("mask", [AR, CH], ids=["ar", "chunk"])
+def test_attention_d80_is_d128_on_zero_padded_heads(E, mode, mask):
+    """At the same scale (1/sqrt(80)), the D = 80 kernel and the D = 128
+    kernel given the same heads zero-padded to 128 dims compute the same
+    scores, the same P and the same dims 0..79 of O: bitwise equal O and
+    LSE."""
+    E.config(*mode)
+    nq, nk, q0, h, hk = 150, 333, 183, 8, 2
+    kw = dict(n_ar=100) if mask == AR else dict(n_prefix=40, chunk_len=70)
+    q, k, v = _qkv(60, nq, nk, h, hk, 80, "bf16")
+    outs = []
+    for d in (80, 128):
+        pad = lambda t: np.pad(t.bits, ((0, 0), (0, 0), (0, d - 80)))
+        O, L = E.empty((nq, h, d), np.uint16), E.empty((h, nq), np.float32)
+        attention(E, E.array(pad(q)), E.array(pad(k)), E.array(pad(v)), O, mode=mask, q0=q0, lse=L,
+                  scale=1.0 / math.sqrt(80.0), **kw)
+        outs.append((np.array(O[..., :80]), np.array(L)))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1].view(np.uint32), outs[1][1].view(np.uint32))
+    want, _ = oattn.attention(q.f32, k.f32, v.f32, q0, mask, **{**kw, "chunk_len": kw.get("chunk_len", 1)})
+    assert_parity(val(outs[0][0]), want, "bf16", "D = 80")
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
 def test_attention_bf16_strided_packed_views(E, mode):
     """K and V as strided views of one [nk, 3, H, D] buffer (the projection's
     output layout) and Q, O with padded rows."""
