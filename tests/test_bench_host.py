@@ -113,3 +113,13 @@ def test_cpu_baseline_reports_a_bounded_oracle_sample():
     n_ar = W.region_counts(wl.segments)[0]
     # every DM row of every head, as the tiny workload fits the budget
     assert "%d DM query rows" % ((wl.n_tokens - n_ar) * wl.n_heads) in cb["sample"]
+
+
+def test_cpu_baseline_reports_the_fields_of_the_line():
+    """The oracle leg of the bench line (host only): a bounded sample of the
+    480p attention, with the fields the line carries."""
+    b = bench.cpu_baseline(W.BY_NAME["t2v480p_bf16"], budget_s=0.5)
+    assert b["kind"] == "oracle" and b["unit"] == "TFLOP/s"
+    assert b["value"] > 0 and b["single_core_value"] > 0
+    assert isinstance(b["cores"], int) and b["cores"] >= 1
+    assert "rows" in b["sample"] and b["projected_full_workload_s"] > 0
