@@ -130,6 +130,7 @@ class Emu:
         L.emu_config.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.emu_stat.restype = ctypes.c_uint64
         L.emu_stat.argtypes = [ctypes.c_int]
+        L.emu_subset.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64]
         # the C entry points take the argument types the product binding
         # declares for them
         from multimodal_diffusion_transformer_amd import _binding
@@ -144,6 +145,11 @@ class Emu:
         """reverse_waves: False / True, or 2 for a seeded random wave order in
         every phase between barriers."""
         self.lib.emu_config(int(dma_late), int(reverse_waves), int(threads))
+
+    def subset(self, stride=0, offset=0, max_groups=0):
+        """Run only workgroups offset, offset + stride, ... (at most
+        max_groups) of the following launches; stride 0 runs all again."""
+        self.lib.emu_subset(int(stride), int(offset), int(max_groups))
 
     def stat(self, i):
         return int(self.lib.emu_stat(i))

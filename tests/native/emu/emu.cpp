@@ -141,6 +141,9 @@ struct Launch {
   size_t shmem;
   const char* name;
   uint64_t total;
+  // the workgroups this launch runs: flat indices offset, offset + stride,
+  // ... (count of them); all of them unless a subset is configured
+  uint64_t sel_offset = 0, sel_stride = 1, count = 0;
   std::atomic<uint64_t> next{0};
   std::atomic<bool> failed{false};
 };
@@ -149,6 +152,8 @@ struct Config {
   int dma_late = 0;
   int reverse = 0;
   int threads = 8;
+  // run only workgroups sub_offset + i * sub_stride, i < sub_max (0: all)
+  uint64_t sub_stride = 0, sub_offset = 0, sub_max = 0;
 };
 Config g_cfg;
 std::mutex g_mu;
@@ -529,8 +534,9 @@ void worker_main(Launch* L) {
   gdim = Idx{L->grid.x, L->grid.y, L->grid.z};
   for (;;) {
     if (L->failed.load()) break;
-    const uint64_t b = L->next.fetch_add(1);
-    if (b >= L->total) break;
+    const uint64_t i = L->next.fetch_add(1);
+    if (i >= L->count) break;
+    const uint64_t b = L->sel_offset + i * L->sel_stride;
     if (sigsetjmp(w->jb, 1) == 0) {
       w->in_kernel = true;
       run_workgroup(w, b);
@@ -580,7 +586,14 @@ void launch_impl(void (*thunk)(const void*), const void* fn, dim3 grid, dim3 blo
   L.shmem = shmem;
   L.name = name;
   L.total = (uint64_t)grid.x * grid.y * grid.z;
-  const int nt = (int)std::max<uint64_t>(1, std::min<uint64_t>((uint64_t)std::max(1, g_cfg.threads), L.total));
+  L.count = L.total;
+  if (g_cfg.sub_stride) {
+    L.sel_stride = g_cfg.sub_stride;
+    L.sel_offset = g_cfg.sub_offset;
+    L.count = L.sel_offset < L.total ? (L.total - L.sel_offset + L.sel_stride - 1) / L.sel_stride : 0;
+    if (g_cfg.sub_max && L.count > g_cfg.sub_max) L.count = g_cfg.sub_max;
+  }
+  const int nt = (int)std::max<uint64_t>(1, std::min<uint64_t>((uint64_t)std::max(1, g_cfg.threads), L.count));
   std::vector<std::thread> th;
   for (int i = 0; i < nt; ++i) th.emplace_back(worker_main, &L);
   for (auto& t : th) t.join();
@@ -734,6 +747,16 @@ void emu_config(int dma_late, int reverse_waves, int threads) {
   emu::g_cfg.dma_late = dma_late;
   emu::g_cfg.reverse = reverse_waves;
   emu::g_cfg.threads = threads > 0 ? threads : 1;
+}
+
+// Run only workgroups offset, offset + stride, ... (at most max_groups, 0:
+// no limit) of each following launch; stride 0 runs every workgroup again.
+// For checking a full-size launch on sampled workgroups: what the skipped
+// workgroups would write stays as it was.
+void emu_subset(uint64_t stride, uint64_t offset, uint64_t max_groups) {
+  emu::g_cfg.sub_stride = stride;
+  emu::g_cfg.sub_offset = offset;
+  emu::g_cfg.sub_max = max_groups;
 }
 
 // the first failure since the last call, or "" (clears it)

@@ -1,0 +1,166 @@
+"""Full-size attention launches on sampled workgroups, on the CPU emulator.
+
+The launch runs at its real grid and shapes, but the emulator executes only
+a strided sample of its workgroups (tests/native/emu, emu_subset). The
+others are skipped, and the output rows they would write keep their NaN
+fill. Every (row, head) the sample writes is compared with the oracle.
+Launches:
+
+* the 480p text-to-video step's attention: 25,474 tokens, 24 heads of 128,
+  Q, K, V strided views of the packed projection output, Q rotated on load;
+* the same layout at the Super head shape (64 / 8 heads of 80);
+* the streaming chunk against the full rolling cache (1,440 queries,
+  13,218 keys, chunk-causal mask);
+* (MOT_EMU_FULLSIZE=1) the long 480p sequence, 76,954 tokens.
+
+The grid is ordered heaviest first: query tile qt = n_qtiles - 1 - x / H,
+so the small x are the last (ragged) DM tiles and the large x the AR tiles.
+Each launch runs one sample from each end and one strided across the
+middle, so the sample takes the ragged last tile, full DM tiles, the tile
+holding the AR/DM boundary, and causal AR tiles.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as oattn
+from oracle import layout as olayout
+from oracle import mrope as omrope
+from tests import emu_lib
+from tests.gpu_util import assert_parity
+
+pytestmark = pytest.mark.skipif(not os.path.exists(emu_lib.CXX), reason="host clang++ missing")
+pytest.importorskip("multimodal_diffusion_transformer_amd._binding")
+
+AR, CH = W.AR_CAUSAL_DM_FULL, W.CHUNK_CAUSAL_KV
+BM = 128  # query rows per workgroup
+
+
+@pytest.fixture(scope="module")
+def E(tmp_path_factory):
+    e = emu_lib.Emu(emu_lib.build(str(tmp_path_factory.mktemp("emu_full"))))
+    e.config(True, True)  # copies held until their wait, waves in reverse
+    yield e
+    e.subset(0)
+    e.free_all()
+
+
+def _launch_sampled(E, samples, **kw):
+    """One launch per (stride, offset, count) sample, into the same output."""
+    from tests.test_emu_kernels import attention
+    for stride, offset, count in samples:
+        E.subset(stride, offset, count)
+        try:
+            attention(E, **kw)
+        finally:
+            E.subset(0)
+
+
+def _written(O):
+    """(rows, heads) with every output dim written (not NaN), grouped per
+    head; each head's rows must be whole 128-row tiles (the last may be
+    ragged)."""
+    vals = W.bf16_to_f32(np.asarray(O))
+    done = ~np.isnan(vals).any(axis=-1)            # [nq, H]
+    assert not (np.isnan(vals).any(axis=-1) & ~np.isnan(vals).all(axis=-1)).any(), "partly written rows"
+    nq = O.shape[0]
+    per_head = {}
+    for h in range(O.shape[1]):
+        rows = np.nonzero(done[:, h])[0]
+        if len(rows) == 0:
+            continue
+        tiles = np.unique(rows // BM)
+        for t in tiles:
+            want = np.arange(t * BM, min(nq, (t + 1) * BM))
+            assert np.array_equal(rows[(rows >= t * BM) & (rows < (t + 1) * BM)], want), (h, t)
+        per_head[h] = rows
+    return vals, per_head
+
+
+def _samples(n_qtiles, h, mid=6):
+    x_total = n_qtiles * h
+    return [(1, 0, 2),                                            # the last (ragged) DM tile
+            (x_total // mid + 1, h + 3, mid),                     # strided across the middle
+            (h + 1, x_total - 5 * h, 5)]                          # query tiles 4..0: AR rows and the boundary
+
+
+def _packed_case(E, wl, seed):
+    """The step's launch at workload wl: Q, K, V strided views of one packed
+    [N, (H + 2 H_kv) D] buffer, Q rotated on load, K as given."""
+    pos, reg, n_ar = olayout.build(wl.segments)
+    n, h, hk, d = len(reg), wl.n_heads, wl.kv_heads, wl.head_dim
+    q = W.make(seed, W.T_Q, (n, h, d), "bf16")
+    k = W.make(seed, W.T_K, (n, hk, d), "bf16")
+    v = W.make(seed, W.T_V, (n, hk, d), "bf16")
+    Y = E.empty((n, (h + 2 * hk) * d), np.uint16)
+    Y[:, :h * d] = q.bits.reshape(n, h * d)
+    Y[:, h * d:(h + hk) * d] = k.bits.reshape(n, hk * d)
+    Y[:, (h + hk) * d:] = v.bits.reshape(n, hk * d)
+    O = E.array(np.full((n, h, d), 0xFFFF, np.uint16))   # NaN
+    P = E.array(np.ascontiguousarray(pos))
+    qv = Y[:, :h * d].reshape(n, h, d)
+    kv_ = Y[:, h * d:(h + hk) * d].reshape(n, hk, d)
+    vv = Y[:, (h + hk) * d:].reshape(n, hk, d)
+    n_qtiles = (n + BM - 1) // BM
+    g0 = E.stat(1)  # workgroups run so far
+    _launch_sampled(E, _samples(n_qtiles, h), q=qv, k=kv_, v=vv, o=O, mode=AR, n_ar=n_ar, q_pos=P,
+                    sections=wl.sections, theta=wl.theta)
+    ran = E.stat(1) - g0
+    vals, per_head = _written(O)
+    assert len(per_head) >= 4
+    checked = 0
+    for head, rows in sorted(per_head.items()):
+        kvh = head // (h // hk)
+        qr = omrope.apply(q.f32[rows][:, [head]], pos[rows], wl.sections, wl.theta)
+        want = oattn.attention_rows(qr, k.f32[:, [kvh]], v.f32[:, [kvh]], rows, [0], 0, AR, n_ar=n_ar)
+        assert_parity(vals[rows][:, [head]], want, "bf16", "%s head %d, %d rows" % (wl.name, head, len(rows)))
+        checked += len(rows)
+    tiles = {(hd, t) for hd, rows in per_head.items() for t in np.unique(rows // BM)}
+    assert len(tiles) == ran == 2 + 6 + 5  # one (head, query tile) per workgroup run, none elsewhere
+    qt_set = {t for _, t in tiles}
+    # the ragged last tile, causal AR rows, the tile holding the AR/DM boundary
+    assert {n_qtiles - 1, 0, n_ar // BM} <= qt_set, sorted(qt_set)
+    return checked
+
+
+@pytest.mark.parametrize("name", ["t2v480p_bf16", "super_t2v480p_bf16"])
+def test_480p_step_attention_on_sampled_workgroups(E, name):
+    checked = _packed_case(E, W.BY_NAME[name], 35)
+    assert checked >= 8 * BM
+
+
+@pytest.mark.skipif(os.environ.get("MOT_EMU_FULLSIZE") != "1", reason="long 480p: set MOT_EMU_FULLSIZE=1")
+def test_long_480p_attention_on_sampled_workgroups(E):
+    checked = _packed_case(E, W.BY_NAME["t2v480p_long_bf16"], 36)
+    assert checked >= 8 * BM
+
+
+def test_streaming_chunk_against_the_full_cache_on_sampled_workgroups(E):
+    """The streaming call: the newest chunk (1,440 rows) against the rolling
+    cache [prefix 258 | 8 history frames | chunk], chunk-causal mask, Q
+    rotated on load at the chunk's positions."""
+    wl = W.BY_NAME["stream_chunk_bf16"]
+    pos, reg, n_ar = olayout.build(wl.segments)
+    nk, h, d = len(reg), wl.n_heads, wl.head_dim
+    ft = wl.stream_views * wl.stream_gh * wl.stream_gw
+    n_prefix = wl.stream_text + 2
+    q0 = nk - ft
+    q = W.make(38, W.T_Q, (ft, h, d), "bf16")
+    k = W.make(38, W.T_K, (nk, h, d), "bf16")
+    v = W.make(38, W.T_V, (nk, h, d), "bf16")
+    qpos = np.ascontiguousarray(pos[q0:])
+    O = E.array(np.full((ft, h, d), 0xFFFF, np.uint16))
+    n_qtiles = (ft + BM - 1) // BM
+    _launch_sampled(E, [(n_qtiles * h // 5 + 1, 2, 5), (1, 0, 1), (1, n_qtiles * h - 1, 1)],
+                    q=E.array(q.bits), k=E.array(k.bits), v=E.array(v.bits), o=O, mode=CH, q0=q0,
+                    n_prefix=n_prefix, chunk_len=ft, q_pos=E.array(qpos), sections=wl.sections,
+                    theta=wl.theta)
+    vals, per_head = _written(O)
+    assert len(per_head) >= 3
+    for head, rows in sorted(per_head.items()):
+        qr = omrope.apply(q.f32[rows][:, [head]], qpos[rows], wl.sections, wl.theta)
+        want = oattn.attention_rows(qr, k.f32[:, [head]], v.f32[:, [head]], rows, [0], q0, CH,
+                                    n_prefix=n_prefix, chunk_len=ft)
+        assert_parity(vals[rows][:, [head]], want, "bf16", "stream head %d, %d rows" % (head, len(rows)))
