@@ -164,3 +164,90 @@ def test_streaming_chunk_against_the_full_cache_on_sampled_workgroups(E):
         want = oattn.attention_rows(qr, k.f32[:, [head]], v.f32[:, [head]], rows, [0], q0, CH,
                                     n_prefix=n_prefix, chunk_len=ft)
         assert_parity(vals[rows][:, [head]], want, "bf16", "stream head %d, %d rows" % (head, len(rows)))
+
+
+def test_480p_projections_on_sampled_workgroups(E):
+    """The step's two region-split projections at 480p: QKV [25,474 x 3,072]
+    x [3,072 x 9,216] and O [25,474 x 3,072] x [3,072 x 3,072], the first
+    514 rows through the Reasoner's weights.  Both rooms' tiles are in the
+    sample (the grid lists the AR problem's tiles first); each written
+    128 x 128 output tile is compared with the oracle at the stored-bf16
+    bound."""
+    from tests.gpu_util import assert_parity_stored
+    from tests.test_emu_kernels import region_linear
+    from oracle import projection as oproj
+    wl = W.BY_NAME["t2v480p_bf16"]
+    n, hid, h, d = wl.n_tokens, wl.hidden, wl.n_heads, wl.head_dim
+    n_ar = W.region_counts(wl.segments)[0]
+    X = W.make(wl.wid, W.T_X, (n, hid), "bf16")
+    for name, tid_ar, tid_dm, d_in, d_out in (("qkv", W.T_WQKV_AR, W.T_WQKV_DM, hid, 3 * h * d),
+                                              ("o", W.T_WO_AR, W.T_WO_DM, h * d, hid)):
+        wa = W.make(wl.wid, tid_ar, (d_in, d_out), "bf16", 0.02)
+        wd = W.make(wl.wid, tid_dm, (d_in, d_out), "bf16", 0.02)
+        x = X if d_in == hid else W.make(wl.wid, W.T_Q, (n, d_in), "bf16")
+        Y = E.array(np.full((n, d_out), 0xFFFF, np.uint16))
+        tn = d_out // 128
+        ar_tiles = (n_ar + 127) // 128 * tn
+        total = ar_tiles + (n - n_ar + 127) // 128 * tn
+        Xe, WA, WD = E.array(x.bits), E.array(wa.bits), E.array(wd.bits)
+        for stride, offset, count in ((tn + 1, 0, (ar_tiles + tn) // (tn + 1)),   # the AR problem
+                                      (total // 8 + 1, ar_tiles, 8),             # the DM problem
+                                      (1, total - 2, 2)):                        # its last (ragged) row tile
+            E.subset(stride, offset, count)
+            try:
+                region_linear(E, Xe, WA, WD, Y, n_ar, 0, 0)
+            finally:
+                E.subset(0)
+        got = W.bf16_to_f32(np.asarray(Y))
+        done = ~np.isnan(got)
+        rows = np.nonzero(done.any(axis=1))[0]
+        assert (rows < n_ar).any() and (rows >= n_ar).any() and rows[-1] == n - 1, name
+        checked = 0
+        # row tiles: 128-row tiles of each room (AR rows [0, n_ar), DM rows
+        # from n_ar), the last of each possibly ragged
+        tile_of = np.where(rows < n_ar, rows // 128, (n_ar + 127) // 128 + (rows - n_ar) // 128)
+        for t in np.unique(tile_of):
+            r0 = t * 128 if t < (n_ar + 127) // 128 else n_ar + (t - (n_ar + 127) // 128) * 128
+            r1 = min(n_ar if r0 < n_ar else n, r0 + 128)
+            rr = np.arange(r0, r1)
+            for c0 in np.unique(np.nonzero(done[rr].any(axis=0))[0] // 128) * 128:
+                blk = got[np.ix_(rr, np.arange(c0, c0 + 128))]
+                assert not np.isnan(blk).any(), (name, r0, c0)   # whole tiles
+                # a tile never straddles the room boundary: each row's room
+                want = np.concatenate([oproj.project_rows(x.f32[rr[rr < n_ar]], wa.f32[:, c0:c0 + 128]),
+                                       oproj.project_rows(x.f32[rr[rr >= n_ar]], wd.f32[:, c0:c0 + 128])])
+                assert_parity_stored(blk, want, "%s tile (%d, %d)" % (name, r0, c0))
+                checked += 1
+        assert checked >= 10, (name, checked)
+
+
+def test_480p_mrope_and_euler_whole_launches(E):
+    """The step's two bandwidth kernels at 480p, every workgroup: mRoPE of K
+    in the packed projection output (25,474 tokens x 24 heads, in place,
+    strided view) and the Euler update of the 24,960 x 3,072 latent with its
+    bf16 mirror."""
+    from oracle import euler as oeuler
+    import ctypes
+    wl = W.BY_NAME["t2v480p_bf16"]
+    pos, reg, n_ar = olayout.build(wl.segments)
+    n, h, d, hid = len(reg), wl.n_heads, wl.head_dim, wl.hidden
+    k = W.make(40, W.T_K, (n, h, d), "bf16")
+    Y = E.empty((n, 3, h, d), np.uint16)
+    Y[:, 1] = k.bits
+    P = E.array(np.ascontiguousarray(pos))
+    view = Y[:, 1]
+    st = E.call("mrope_apply", emu_lib.ptr(view), 0, n, h, d, 3 * h * d, d, emu_lib.ptr(P), *wl.sections,
+                ctypes.c_float(wl.theta), None)
+    assert st == 0
+    assert_parity(W.bf16_to_f32(np.asarray(Y[:, 1])), omrope.apply(k.f32, pos, wl.sections, wl.theta), "bf16",
+                  "mrope K 480p")
+    assert (Y[:, 0] == 0).all() and (Y[:, 2] == 0).all()   # Q and V untouched
+    n_noisy = W.region_counts(wl.segments)[2]
+    x0 = W.make(wl.wid, W.T_LATENT, (n_noisy * hid,), "fp32").f32
+    v = W.make(41, 1, (n_noisy * hid,), "bf16")
+    X, V, XB = E.array(x0), E.array(v.bits), E.empty((n_noisy * hid,), np.uint16)
+    st = E.call("flow_euler_step", emu_lib.ptr(X), emu_lib.ptr(V), 0, n_noisy * hid, ctypes.c_float(1.0),
+                ctypes.c_float(0.975), emu_lib.ptr(XB), None)
+    assert st == 0
+    assert_parity(np.asarray(X), oeuler.step(x0, v.f32, 1.0, 0.975), "fp32", "euler 480p")
+    np.testing.assert_array_equal(np.asarray(XB), W.bf16_bits(np.asarray(X)))
