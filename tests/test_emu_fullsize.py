@@ -166,21 +166,26 @@ def test_streaming_chunk_against_the_full_cache_on_sampled_workgroups(E):
         assert_parity(vals[rows][:, [head]], want, "bf16", "stream head %d, %d rows" % (head, len(rows)))
 
 
-def test_480p_projections_on_sampled_workgroups(E):
-    """The step's two region-split projections at 480p: QKV [25,474 x 3,072]
-    x [3,072 x 9,216] and O [25,474 x 3,072] x [3,072 x 3,072], the first
-    514 rows through the Reasoner's weights.  Both rooms' tiles are in the
-    sample (the grid lists the AR problem's tiles first); each written
-    128 x 128 output tile is compared with the oracle at the stored-bf16
-    bound."""
+@pytest.mark.parametrize("name", ["t2v480p_bf16", "super_t2v480p_bf16",
+                                  pytest.param("t2v480p_long_bf16", marks=pytest.mark.skipif(
+                                      os.environ.get("MOT_EMU_FULLSIZE") != "1",
+                                      reason="long 480p: set MOT_EMU_FULLSIZE=1"))])
+def test_480p_projections_on_sampled_workgroups(E, name):
+    """The step's two region-split projections at full size, the first 514
+    rows through the Reasoner's weights: at 480p QKV [25,474 x 3,072] x
+    [3,072 x 9,216] and O [25,474 x 3,072] x [3,072 x 3,072]; the Super
+    heads' [.. x 5,120] x [5,120 x 6,400] and x [5,120 x 5,120]; the long
+    sequence's 76,954 rows.  Both rooms' tiles are in the sample (the grid
+    lists the AR problem's tiles first); each written 128 x 128 output tile
+    is compared with the oracle at the stored-bf16 bound."""
     from tests.gpu_util import assert_parity_stored
     from tests.test_emu_kernels import region_linear
     from oracle import projection as oproj
-    wl = W.BY_NAME["t2v480p_bf16"]
-    n, hid, h, d = wl.n_tokens, wl.hidden, wl.n_heads, wl.head_dim
+    wl = W.BY_NAME[name]
+    n, hid, h, d, hk = wl.n_tokens, wl.hidden, wl.n_heads, wl.head_dim, wl.kv_heads
     n_ar = W.region_counts(wl.segments)[0]
     X = W.make(wl.wid, W.T_X, (n, hid), "bf16")
-    for name, tid_ar, tid_dm, d_in, d_out in (("qkv", W.T_WQKV_AR, W.T_WQKV_DM, hid, 3 * h * d),
+    for name, tid_ar, tid_dm, d_in, d_out in (("qkv", W.T_WQKV_AR, W.T_WQKV_DM, hid, (h + 2 * hk) * d),
                                               ("o", W.T_WO_AR, W.T_WO_DM, h * d, hid)):
         wa = W.make(wl.wid, tid_ar, (d_in, d_out), "bf16", 0.02)
         wd = W.make(wl.wid, tid_dm, (d_in, d_out), "bf16", 0.02)
