@@ -256,3 +256,97 @@ def test_480p_mrope_and_euler_whole_launches(E):
     assert st == 0
     assert_parity(np.asarray(X), oeuler.step(x0, v.f32, 1.0, 0.975), "fp32", "euler 480p")
     np.testing.assert_array_equal(np.asarray(XB), W.bf16_bits(np.asarray(X)))
+
+
+def _tiles_checked(got, want_fn, n, n_ar, d_out, what):
+    """Compare every written 128 x 128 tile of a region GEMM output (rows
+    tiled per room) with want_fn(rows, c0) at the stored-bf16 bound."""
+    from tests.gpu_util import assert_parity_stored
+    done = ~np.isnan(got)
+    rows = np.nonzero(done.any(axis=1))[0]
+    n_ar_t = (n_ar + 127) // 128
+    tile_of = np.where(rows < n_ar, rows // 128, n_ar_t + (rows - n_ar) // 128)
+    checked = 0
+    for t in np.unique(tile_of):
+        r0 = t * 128 if t < n_ar_t else n_ar + (t - n_ar_t) * 128
+        rr = np.arange(r0, min(n_ar if r0 < n_ar else n, r0 + 128))
+        for c0 in np.unique(np.nonzero(done[rr].any(axis=0))[0] // 128) * 128:
+            blk = got[np.ix_(rr, np.arange(c0, min(d_out, c0 + 128)))]
+            assert not np.isnan(blk).any(), (what, r0, c0)
+            assert_parity_stored(blk, want_fn(rr, c0), "%s tile (%d, %d)" % (what, r0, c0))
+            checked += 1
+    return checked
+
+
+@pytest.mark.skipif(os.environ.get("MOT_EMU_FULLSIZE") != "1", reason="whole-layer kernels: set MOT_EMU_FULLSIZE=1")
+@pytest.mark.parametrize("name", ["nano_t2v480p_bf16", "super_t2v480p_bf16"])
+def test_layer_kernels_at_480p(E, name):
+    """The rest of the layer at the model table's shapes on the 480p layout
+    (25,474 rows): LayerNorm of every row (whole launch), the MLP up
+    projection with its GELU epilogue and the down projection with its
+    residual epilogue on sampled tiles of both rooms, and the guided Euler
+    update of the whole latent (whole launch)."""
+    import ctypes
+    from tests.test_emu_kernels import region_linear
+    from oracle import block as oblock
+    from oracle import cfg as ocfg
+    from oracle import projection as oproj
+    wl = W.BY_NAME[name]
+    n, hid, ffn = wl.n_tokens, wl.hidden, wl.ffn
+    n_ar, _, n_noisy = W.region_counts(wl.segments)
+    p = W.block_params(wl)
+    X = W.make(wl.wid, W.T_X, (n, hid), "bf16")
+    # LayerNorm, every row
+    U = E.empty((n, hid), np.uint16)
+    (ga, ba), (gd, bd) = p["ln1_ar"], p["ln1_dm"]
+    st = E.call("mot_layernorm_region", emu_lib.ptr(E.array(X.bits)), emu_lib.ptr(U), n, n_ar, hid,
+                emu_lib.ptr(E.array(ga.f32)), emu_lib.ptr(E.array(ba.f32)), emu_lib.ptr(E.array(gd.f32)),
+                emu_lib.ptr(E.array(bd.f32)), ctypes.c_float(1e-6), 0, 0, None)
+    assert st == 0
+    u = W.bf16_to_f32(np.asarray(U))
+    want_u = oblock.region_layer_norm(X.f32, (ga.f32, ba.f32), (gd.f32, bd.f32), n_ar, 1e-6)
+    assert_parity(u, want_u, "bf16", "%s ln1, every row" % name)
+
+    def sampled(epi, x, wa, wd, d_out, res=None):
+        Y = E.array(np.full((n, d_out), 0xFFFF, np.uint16))
+        R = None if res is None else E.array(res)
+        tn = d_out // 128
+        ar_tiles = (n_ar + 127) // 128 * tn
+        total = ar_tiles + (n - n_ar + 127) // 128 * tn
+        Xe, WA, WD = E.array(x), E.array(wa), E.array(wd)
+        for stride, offset, count in ((tn + 1, 0, 4), (total // 6 + 1, ar_tiles + 5, 6), (1, total - 1, 1)):
+            E.subset(stride, offset, count)
+            try:
+                region_linear(E, Xe, WA, WD, Y, n_ar, 0, 0, epi, R)
+            finally:
+                E.subset(0)
+        return Y
+
+    up_a, up_d = p["up_ar"], p["up_dm"]
+    A = sampled(1, U, up_a.bits, up_d.bits, ffn)
+    a = W.bf16_to_f32(np.asarray(A))
+    room = lambda rr, c0, wa_, wd_, x_: np.concatenate(
+        [oproj.project_rows(x_[rr[rr < n_ar]], wa_[:, c0:c0 + 128]),
+         oproj.project_rows(x_[rr[rr >= n_ar]], wd_[:, c0:c0 + 128])])
+    k1 = _tiles_checked(a, lambda rr, c0: oblock.gelu(room(rr, c0, up_a.f32, up_d.f32, u)), n, n_ar, ffn,
+                        "%s mlp up + gelu" % name)
+    # the down projection over a full activation block, with the residual
+    A_full = W.make(wl.wid, 60, (n, ffn), "bf16")
+    H1 = W.make(wl.wid, 61, (n, hid), "bf16", 4.0)
+    dn_a, dn_d = p["down_ar"], p["down_dm"]
+    H2 = sampled(2, A_full.bits, dn_a.bits, dn_d.bits, hid, res=H1.bits)
+    h2 = W.bf16_to_f32(np.asarray(H2))
+    k2 = _tiles_checked(h2, lambda rr, c0: H1.f32[np.ix_(rr, np.arange(c0, c0 + 128))] +
+                        room(rr, c0, dn_a.f32, dn_d.f32, A_full.f32), n, n_ar, hid, "%s mlp down + residual" % name)
+    assert k1 >= 8 and k2 >= 8, (k1, k2)
+    # guided Euler, the whole latent
+    m = n_noisy * hid
+    x0 = W.make(wl.wid, W.T_LATENT, (m,), "fp32").f32
+    vc, vb = W.make(62, 1, (m,), "bf16"), W.make(62, 2, (m,), "bf16")
+    Xl, XB = E.array(x0), E.empty((m,), np.uint16)
+    st = E.call("flow_cfg_euler_step", emu_lib.ptr(Xl), emu_lib.ptr(E.array(vc.bits)), emu_lib.ptr(E.array(vb.bits)),
+                0, m, ctypes.c_float(wl.guidance), ctypes.c_float(1.0), ctypes.c_float(0.975), emu_lib.ptr(XB), None)
+    assert st == 0
+    assert_parity(np.asarray(Xl), ocfg.euler_step(x0, vc.f32, vb.f32, wl.guidance, 1.0, 0.975), "fp32",
+                  "%s guided euler" % name)
+    np.testing.assert_array_equal(np.asarray(XB), W.bf16_bits(np.asarray(Xl)))
