@@ -350,3 +350,52 @@ def test_layer_kernels_at_480p(E, name):
     assert_parity(np.asarray(Xl), ocfg.euler_step(x0, vc.f32, vb.f32, wl.guidance, 1.0, 0.975), "fp32",
                   "%s guided euler" % name)
     np.testing.assert_array_equal(np.asarray(XB), W.bf16_bits(np.asarray(Xl)))
+
+
+@pytest.mark.skipif(os.environ.get("MOT_EMU_FULLSIZE") != "1", reason="guided pair at 480p: set MOT_EMU_FULLSIZE=1")
+@pytest.mark.parametrize("name", ["nano_t2v480p_bf16", "super_t2v480p_bf16"])
+def test_guided_pair_attention_at_480p_on_sampled_workgroups(E, name):
+    """Both predictions of a guided step in one launch at 480p: one packed
+    buffer [AR cond | DM | AR base] of (N + n_ar) rows; item 0 reads keys
+    [0, N), item 1 keys [n_ar, n_ar + N) (overlapping views, batch stride
+    n_ar rows); the DM rows' Q shared (batch stride 0), rotated on load."""
+    from tests.test_emu_kernels import attention
+    wl = W.BY_NAME[name]
+    pos, reg, n_ar = olayout.build(wl.segments)
+    n, h, hk, d = len(reg), wl.n_heads, wl.kv_heads, wl.head_dim
+    n_dm = n - n_ar
+    rows_all = n + n_ar
+    width = (h + 2 * hk) * d
+    q = W.make(39, W.T_Q, (n_dm, h, d), "bf16")
+    k = W.make(39, W.T_K, (rows_all, hk, d), "bf16")
+    v = W.make(39, W.T_V, (rows_all, hk, d), "bf16")
+    Y = E.empty((rows_all, width), np.uint16)
+    Y[n_ar:n_ar + n_dm, :h * d] = q.bits.reshape(n_dm, h * d)
+    Y[:, h * d:(h + hk) * d] = k.bits.reshape(rows_all, hk * d)
+    Y[:, (h + hk) * d:] = v.bits.reshape(rows_all, hk * d)
+    st = np.lib.stride_tricks
+    it = Y.itemsize
+    qv = st.as_strided(Y[n_ar:], (2, n_dm, h, d), (0, width * it, d * it, it))
+    kv_ = st.as_strided(Y[:, h * d:], (2, n, hk, d), (n_ar * width * it, width * it, d * it, it))
+    vv = st.as_strided(Y[:, (h + hk) * d:], (2, n, hk, d), (n_ar * width * it, width * it, d * it, it))
+    O = E.array(np.full((2, n_dm, h, d), 0xFFFF, np.uint16))
+    P = E.array(np.ascontiguousarray(pos[n_ar:]))
+    n_qtiles = (n_dm + BM - 1) // BM
+    per_item = n_qtiles * h
+    samples = [(per_item // 4 + 1, 1, 4), (1, per_item - 1, 1),                  # item 0
+               (per_item // 4 + 1, per_item + 3, 4), (1, 2 * per_item - 2, 2)]   # item 1
+    _launch_sampled(E, samples, q=qv, k=kv_, v=vv, o=O, mode=AR, q0=n_ar, n_ar=n_ar, q_pos=P,
+                    sections=wl.sections, theta=wl.theta)
+    checked = 0
+    for b in range(2):
+        vals, per_head = _written(O[b])
+        assert per_head, b
+        keys = slice(b * n_ar, b * n_ar + n)
+        for head, rows in sorted(per_head.items()):
+            kvh = head // (h // hk)
+            qr = omrope.apply(q.f32[rows][:, [head]], pos[n_ar + rows], wl.sections, wl.theta)
+            want = oattn.attention_rows(qr, k.f32[keys][:, [kvh]], v.f32[keys][:, [kvh]], n_ar + rows, [0], 0, AR,
+                                        n_ar=n_ar)
+            assert_parity(vals[rows][:, [head]], want, "bf16", "%s item %d head %d" % (name, b, head))
+            checked += len(rows)
+    assert checked >= 8 * BM
