@@ -166,10 +166,11 @@ def test_streaming_chunk_against_the_full_cache_on_sampled_workgroups(E):
         assert_parity(vals[rows][:, [head]], want, "bf16", "stream head %d, %d rows" % (head, len(rows)))
 
 
-@pytest.mark.parametrize("name", ["t2v480p_bf16", "super_t2v480p_bf16",
-                                  pytest.param("t2v480p_long_bf16", marks=pytest.mark.skipif(
-                                      os.environ.get("MOT_EMU_FULLSIZE") != "1",
-                                      reason="long 480p: set MOT_EMU_FULLSIZE=1"))])
+BY_HAND = pytest.mark.skipif(os.environ.get("MOT_EMU_FULLSIZE") != "1", reason="set MOT_EMU_FULLSIZE=1")
+
+
+@pytest.mark.parametrize("name", ["t2v480p_bf16", pytest.param("super_t2v480p_bf16", marks=BY_HAND),
+                                  pytest.param("t2v480p_long_bf16", marks=BY_HAND)])
 def test_480p_projections_on_sampled_workgroups(E, name):
     """The step's two region-split projections at full size, the first 514
     rows through the Reasoner's weights: at 480p QKV [25,474 x 3,072] x
