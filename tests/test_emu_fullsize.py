@@ -400,3 +400,52 @@ def test_guided_pair_attention_at_480p_on_sampled_workgroups(E, name):
             assert_parity(vals[rows][:, [head]], want, "bf16", "%s item %d head %d" % (name, b, head))
             checked += len(rows)
     assert checked >= 8 * BM
+
+
+def test_streaming_chunk_key_split_and_merge_on_sampled_workgroups(E):
+    """The streaming call with its keys split in two (the key-split path of
+    the streaming cache): one launch of two items over the two halves of the
+    13,218-key cache, Q shared, each half plain full attention (the chunk is
+    the newest); the sample runs the same (query tile, head) workgroups of
+    both items; then mot_attention_merge of all rows.  The merged rows of
+    the sampled tiles are compared with attention over all keys."""
+    wl = W.BY_NAME["stream_chunk_bf16"]
+    pos, reg, _ = olayout.build(wl.segments)
+    nk, h, d = len(reg), wl.n_heads, wl.head_dim
+    ft = wl.stream_views * wl.stream_gh * wl.stream_gw
+    n_prefix = wl.stream_text + 2
+    q0 = nk - ft
+    half = nk // 2
+    q = W.make(42, W.T_Q, (ft, h, d), "bf16")
+    k = W.make(42, W.T_K, (nk, h, d), "bf16")
+    v = W.make(42, W.T_V, (nk, h, d), "bf16")
+    qpos = np.ascontiguousarray(pos[q0:])
+    Q, K, V = E.array(q.bits), E.array(k.bits), E.array(v.bits)
+    st = np.lib.stride_tricks
+    Qb = st.as_strided(Q, (2, ft, h, d), (0,) + Q.strides)
+    Kb = st.as_strided(K, (2, half, h, d), (half * K.strides[0],) + K.strides)
+    Vb = st.as_strided(V, (2, half, h, d), (half * V.strides[0],) + V.strides)
+    Op = E.array(np.full((2, ft, h, d), 0xFFFF, np.uint16))
+    Lp = E.array(np.full((2, h, ft), np.nan, np.float32))
+    per_item = ((ft + BM - 1) // BM) * h
+    # the same workgroup of both items: offsets x and x + per_item
+    _launch_sampled(E, [(per_item, x, 2) for x in (0, 7, per_item // 2 + 5, per_item - 1)], q=Qb, k=Kb, v=Vb,
+                    o=Op, mode=AR, q0=0, n_ar=0, q_pos=E.array(qpos), sections=wl.sections, theta=wl.theta,
+                    lse=Lp)
+    O = E.array(np.full((ft, h, d), 0xFFFF, np.uint16))
+    L = E.array(np.full((h, ft), np.nan, np.float32))
+    el = [s_ // Op.itemsize for s_ in Op.strides]
+    st_ = E.call("mot_attention_merge", emu_lib.ptr(Op), emu_lib.ptr(Lp), 2, el[0], ft, h, d, el[1], el[2],
+                 emu_lib.ptr(O), h * d, d, emu_lib.ptr(L), 0, None)
+    assert st_ == 0
+    _, parts = _written(Op[0])
+    vals = W.bf16_to_f32(np.asarray(O))
+    checked = 0
+    for head, rows in sorted(parts.items()):
+        assert not np.isnan(W.bf16_to_f32(np.asarray(Op[1]))[rows][:, head]).any()   # both halves ran
+        qr = omrope.apply(q.f32[rows][:, [head]], qpos[rows], wl.sections, wl.theta)
+        want = oattn.attention_rows(qr, k.f32[:, [head]], v.f32[:, [head]], rows, [0], q0, CH,
+                                    n_prefix=n_prefix, chunk_len=ft)
+        assert_parity(vals[rows][:, [head]], want, "bf16", "split + merge head %d" % head)
+        checked += len(rows)
+    assert checked >= 2 * BM
