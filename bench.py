@@ -581,6 +581,22 @@ def _counter_mean(d, kernel, counter):
     return sum(per.values()) / len(per), len(per)
 
 
+def attention_work_text(workload):
+    """The algorithmic work of one attention launch of `workload`, as text:
+    the allowed (query, key) pairs x heads x 4 D flop (the streaming chunk
+    is the newest, so each of its rows sees every cached key)."""
+    import workloads as W
+    wl = W.BY_NAME[workload]
+    n, h, d = wl.n_tokens, wl.n_heads, wl.head_dim
+    if wl.mask == W.CHUNK_CAUSAL_KV:
+        ft = wl.stream_views * wl.stream_gh * wl.stream_gw
+        pairs = ft * n
+    else:
+        pairs = attention_pairs(n, W.region_counts(wl.segments)[0])
+    return "%.3f TFLOP per launch (%s allowed pairs x %d heads x %d flop)" % (
+        4.0 * d * h * pairs / 1e12, format(pairs, ","), h, 4 * d)
+
+
 def write_profiles(d, workload):
     """Write profiles/<kernel>_<workload>_{kernel_stats,hbm_traffic,sq_counters}.txt
     from the rocprofv3 CSV runs under d (the commands are recorded in each)."""
@@ -589,8 +605,7 @@ def write_profiles(d, workload):
                 "<out> the output folder):\n  cd /tmp && export TMPDIR=/tmp\n")
     bench = "python3 <repo>/bench.py --workload %s" % workload
     h = attention_kernel_hash()
-    flops = "7.815 TFLOP per launch (635,963,395 allowed pairs x 24 heads x 512 flop)" \
-        if workload == "t2v480p_bf16" else "see DESIGN"
+    flops = attention_work_text(workload)
     # 1. kernel durations
     txt = ("Kernel durations of one benchmark run of %s; one step = QKV projection, mRoPE of K,\n"
            "attention (Q rotated on load), O projection, Euler update.\n\n" % workload + cmd_head +

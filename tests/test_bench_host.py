@@ -21,6 +21,13 @@ def test_attention_pairs_equal_the_mask_count(name):
     assert bench.attention_pairs(n, n_ar) == omask.count_pairs(n, n, 0, W.AR_CAUSAL_DM_FULL, n_ar=n_ar)
 
 
+def test_profile_work_text_names_the_launchs_flops():
+    assert bench.attention_work_text("t2v480p_bf16") == \
+        "7.815 TFLOP per launch (635,963,395 allowed pairs x 24 heads x 512 flop)"
+    # the streaming chunk: 1,440 rows x 13,218 keys
+    assert bench.attention_work_text("stream_chunk_bf16").startswith("0.234 TFLOP per launch (19,033,920 ")
+
+
 def test_480p_flops_per_launch():
     wl = W.BY_NAME["t2v480p_bf16"]
     n, n_ar = wl.n_tokens, W.region_counts(wl.segments)[0]
