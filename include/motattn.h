@@ -235,9 +235,11 @@ typedef struct {
 /* Flash-style masked attention, O = softmax(mask(Q K^T * scale)) V per head
  * (method page §3 equations; streaming page for the chunk mode).  bf16 runs
  * on MFMA with fp32 online softmax and skips tiles with no allowed pair;
- * fp32 runs on the vector ALUs in fp32.  Requires nq >= 1, nk >= q0 + nq in
- * AR mode (every query sees its diagonal), q0 >= n_prefix and chunk_len >= 1
- * in chunk mode, 0 <= n_ar, n_prefix <= nk.  bf16 returns
+ * fp32 runs on the vector ALUs in fp32.  nq == 0 is a no-op that touches
+ * nothing (null pointers allowed; INVALID_ARG for a bad dtype, head count or
+ * size, nk < 0 or q0 < 0).  Otherwise requires nk >= q0 + nq
+ * in AR mode (every query sees its diagonal), q0 >= n_prefix and chunk_len >=
+ * 1 in chunk mode, 0 <= n_ar, n_prefix <= nk, nk >= 1.  bf16 returns
  * MOT_ERR_UNSUPPORTED when k_pos is set (bf16 rotates Q on load only: rotate
  * K beforehand with mrope_apply, which is also the layout a key cache keeps),
  * when nk > 2^31 - 65 or nq > 2^31 - 1, or when a 64-row tile of K or V

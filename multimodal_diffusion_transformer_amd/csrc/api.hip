@@ -80,9 +80,12 @@ extern "C" const char* mot_status_string(int32_t s) {
 
 extern "C" mot_status mot_attention_fwd(const mot_attn_args* a, void* stream) {
   if (!a) return MOT_ERR_INVALID_ARG;
-  if (!a->q || !a->k || !a->v || !a->o) return MOT_ERR_INVALID_ARG;
   if (a->n_heads <= 0 || (a->head_dim != 64 && a->head_dim != 80 && a->head_dim != 128)) return MOT_ERR_INVALID_ARG;
   if (a->dt != MOT_BF16 && a->dt != MOT_FP32) return MOT_ERR_INVALID_ARG;
+  // no query rows: a no-op that touches nothing (null pointers allowed), like
+  // the other calls' empty inputs
+  if (a->nq == 0) return a->nk >= 0 && a->q0 >= 0 ? MOT_OK : MOT_ERR_INVALID_ARG;
+  if (!a->q || !a->k || !a->v || !a->o) return MOT_ERR_INVALID_ARG;
   if (!mask_args_ok(a)) return MOT_ERR_INVALID_ARG;
   if (!(a->scale >= 0.f) || !isfinite(a->scale)) return MOT_ERR_INVALID_ARG;
   const int64_t al = a->dt == MOT_BF16 ? 8 : 4;

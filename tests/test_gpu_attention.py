@@ -248,6 +248,23 @@ def test_attention_chunk_rows_bitwise_invariant_to_future_chunks():
     assert not torch.equal(a[c:], b[c:])
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_attention_with_no_query_rows_is_a_no_op(dtype):
+    """An empty query block (and an empty LSE) through the binding: the
+    call returns and writes nothing."""
+    dev = device()
+    mot = _mot()
+    h, d, nk = 2, 128, 70
+    k = torch.ones((nk, h, d), dtype=dtype, device=dev)
+    q = torch.empty((0, h, d), dtype=dtype, device=dev)
+    o = torch.empty((0, h, d), dtype=dtype, device=dev)
+    lse = torch.empty((h, 0), dtype=torch.float32, device=dev)
+    guard = torch.full((4,), 7.0, device=dev)
+    mot.mot_attention_fwd(q, k, k, o, mask=mot.MOT_AR_CAUSAL_DM_FULL, n_ar=10, lse=lse)
+    torch.cuda.synchronize()
+    assert o.numel() == 0 and torch.equal(guard, torch.full((4,), 7.0, device=dev))
+
+
 def test_attention_first_row_is_first_value_exactly():
     dev = device()
     mot = _mot()

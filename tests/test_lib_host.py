@@ -192,7 +192,8 @@ def _args(**kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(q=None), dict(head_dim=96), dict(n_heads=0), dict(nq=0), dict(nk=10),
+    dict(q=None), dict(head_dim=96), dict(n_heads=0), dict(nq=-1), dict(nk=10), dict(nq=0, nk=-1),
+    dict(nq=0, head_dim=96),
     dict(q_ts=7), dict(o_hs=0), dict(q=4100), dict(dt=5), dict(mask=7),
     dict(mask=mot.MOT_CHUNK_CAUSAL_KV, chunk_len=0),
     dict(mask=mot.MOT_CHUNK_CAUSAL_KV, chunk_len=8, n_prefix=10, q0=5, nk=100),
@@ -217,6 +218,14 @@ def test_attention_rejects_bad_args(kw):
 def test_attention_bf16_unsupported(kw):
     st = mot.raw_call("mot_attention_fwd", ctypes.byref(_args(**kw)), None)
     assert st == mot.MOT_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dt", [mot.MOT_BF16, mot.MOT_FP32])
+def test_attention_with_no_query_rows_is_a_no_op(dt):
+    # the pointers are never dereferenced: nothing is launched
+    for kw in (dict(nq=0), dict(nq=0, nk=0), dict(nq=0, mask=mot.MOT_CHUNK_CAUSAL_KV, chunk_len=0),
+               dict(nq=0, q=None, o=None)):
+        assert mot.raw_call("mot_attention_fwd", ctypes.byref(_args(dt=dt, **kw)), None) == mot.MOT_OK
 
 
 def test_launches_past_one_dispatch_are_unsupported():
