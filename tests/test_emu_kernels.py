@@ -344,12 +344,13 @@ def test_attention_fp32(E, case):
     np.testing.assert_allclose(L, lse, atol=1e-4, rtol=0)
 
 
-def test_attention_fp32_batched_rope_both(E):
+@pytest.mark.parametrize("d", [64, 80])
+def test_attention_fp32_batched_rope_both(E, d):
     """fp32 with two batch items, GQA and mRoPE on load for Q and K."""
     E.config(False, False)
-    n, h, hk, d = 120, 4, 2, 64
+    n, h, hk = 120, 4, 2
     pos = np.ascontiguousarray(olayout.build(W.BY_NAME["policy_bf16"].segments)[0][:n])
-    secs = (8, 12, 12)
+    secs = (d // 8, 3 * d // 16, 3 * d // 16)
     ins = [_qkv(40 + b, n, n, h, hk, d, "fp32") for b in range(2)]
     Q = E.array(np.stack([t[0].f32 for t in ins]))
     K = E.array(np.stack([t[1].f32 for t in ins]))
