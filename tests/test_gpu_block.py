@@ -154,10 +154,26 @@ def _model_on(model, layout_name):
     return dataclasses.replace(m, name="%s_on_%s" % (model, layout_name), segments=base.segments)
 
 
+_PARAMS = {}
+
+
+def _params(wl):
+    """The seeded layer parameters depend on the workload id and the model
+    shape only, not the layout: each model shape's set is drawn once for the
+    tests that use it (the Super shape's are 642 M elements, the Nano
+    shape's 285 M)."""
+    key = (wl.wid, wl.n_heads, wl.head_dim, wl.hidden, wl.kv_heads, wl.ffn, wl.dtype)
+    if key not in _PARAMS:
+        if len(_PARAMS) >= 2:
+            _PARAMS.clear()
+        _PARAMS[key] = W.block_params(wl)
+    return _PARAMS[key]
+
+
 def _block(wl, dev):
     from multimodal_diffusion_transformer_amd import pipeline
     X = W.make(wl.wid, W.T_X, (wl.n_tokens, wl.hidden), wl.dtype)
-    params = W.block_params(wl)
+    params = _params(wl)
     tp = {k: (tuple(W.to_torch(t) for t in v) if k.startswith("ln") else W.to_torch(v))
           for k, v in params.items()}
     blk = pipeline.BlockStep(wl, W.to_torch(X), tp, device=dev)
