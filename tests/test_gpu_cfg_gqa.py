@@ -197,6 +197,27 @@ def test_attention_grouped_heads(case):
                        O2.view(torch.int16) if dtype == "bf16" else O2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_mrope_at_head_size_80(dtype):
+    """Standalone mRoPE at the Super head size (40 pairs in t / h / w
+    sections of 10 / 15 / 15; 25 tokens per workgroup, the last lanes idle)
+    on the K view of a packed [N, 64 + 16, 80] projection output."""
+    dev = device()
+    mot = _mot()
+    wl = W.BY_NAME["super_t2v480p_bf16"]
+    pos, reg, n_ar = olayout.build(W.BY_NAME["policy_bf16"].segments)
+    n, h, hk, d = len(reg), wl.n_heads, wl.kv_heads, wl.head_dim
+    y = _rand(38, 1, (n, h + 2 * hk, d), dtype)
+    Y = W.to_torch(y, dev).contiguous()
+    mot.mrope_apply(Y[:, h:h + hk], torch.from_numpy(pos).to(dev), wl.sections, wl.theta)
+    torch.cuda.synchronize()
+    got = to_np(Y)
+    assert_parity(got[:, h:h + hk], omrope.apply(y.f32[:, h:h + hk], pos, wl.sections, wl.theta), dtype,
+                  "mrope D = 80")
+    np.testing.assert_array_equal(got[:, :h], y.f32[:, :h])
+    np.testing.assert_array_equal(got[:, h + hk:], y.f32[:, h + hk:])
+
+
 @pytest.mark.parametrize("mode", [AR, CH], ids=["ar", "chunk"])
 def test_attention_d80_is_d128_on_zero_padded_heads(mode):
     """Head size 80 (the model table's Super heads) runs the D = 128

@@ -20,7 +20,8 @@ def _mot():
     return mot
 
 
-@pytest.mark.parametrize("dtype,d,parts", [("bf16", 128, 2), ("bf16", 64, 3), ("fp32", 128, 2), ("fp32", 64, 1)])
+@pytest.mark.parametrize("dtype,d,parts", [("bf16", 128, 2), ("bf16", 64, 3), ("fp32", 128, 2), ("fp32", 64, 1),
+                                           ("bf16", 80, 3)])
 def test_merge_parity(dtype, d, parts):
     dev = device()
     mot = _mot()
