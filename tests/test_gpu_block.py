@@ -181,6 +181,7 @@ def _block(wl, dev):
     return blk, X, pf
 
 
+@pytest.mark.timeout(900)  # the Super shape draws 642 M parameters and runs a 1.3 TFLOP fp64 oracle layer
 @pytest.mark.parametrize("model", ["nano", "super"])
 def test_block_forward_policy_layout_teacher_forced(model):
     dev = device()
@@ -237,6 +238,7 @@ def test_block_forward_policy_layout_teacher_forced(model):
     assert rl <= BF16_REL_L2
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["nano_t2v480p_bf16", "super_t2v480p_bf16"])
 def test_block_forward_480p_sampled_rows(name):
     """The whole layer at the grouped-head 480p workloads (25,474 tokens;

@@ -304,6 +304,7 @@ def _guided_step(wl, guidance, dev):
     return g, X, Xb, ws, x
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,guidance,steps,checked", [("policy_bf16", 3.0, 10, (0, 1, 9)),
                                                          ("tiny_fp32", 6.0, 1, (0,)),
                                                          ("super_on_policy_bf16", 3.0, 2, (0, 1))])

@@ -83,6 +83,7 @@ def _assert_walked(sig, pairs, n, shift):
     assert pairs == [(float(want[k]), float(want[k + 1])) for k in range(n)]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny_fp32", "policy_bf16"])
 def test_guided_loop_robot_policy_setting(name):
     dev = device()
